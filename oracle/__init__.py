@@ -1,0 +1,36 @@
+"""fp64 CPU oracle for the Fast-dLLM block-decoding hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+the benchmark's CPU-baseline leg may import this package.  The HIP library
+never calls it and must fail loudly when its own extension is missing.
+
+It shares no code with the HIP path: no kernels, headers, helpers, tables or
+pre/post-processing.  Inputs come from ``workloads`` (seeded generators that
+hold none of the method's arithmetic).
+
+Parity status of each function (pins live in tests/test_oracle_*.py):
+
+* ``fresh_range``       pinned (closed form per mode, hand-checked cases)
+* ``attn_ref``          pinned (SDPA in float64, closed forms, hand-computed
+                        golden fixture, post-refresh identity, nested-mode
+                        equalities, GQA==MHA, batch permutation)
+* ``row_confidence``    pinned (scipy softmax, sigmoid identity, calibrated
+                        recipe, hand-computed golden fixture)
+* ``unmask_ref``        pinned (brute force over all masks for tiny blocks,
+                        tau>=1 -> one token, tau below all -> whole block,
+                        monotonicity, hand-computed golden fixture)
+* ``refresh_ref``       pinned (bit-exact copy, sentinel, idempotence, subset)
+* ``decode_block_ref``  pinned (step counts 1..m, tau>=1 -> m steps)
+* model-level quality (accuracy, real staleness drift, Theorem 1):
+  parity unpinned -- needs trained weights and datasets, out of scope.
+"""
+from .fdllm_oracle import (  # noqa: F401
+    fresh_range,
+    attn_ref,
+    row_confidence,
+    unmask_ref,
+    UnmaskResult,
+    refresh_ref,
+    decode_block_ref,
+    NEAR_TIE,
+)
