@@ -1,0 +1,10 @@
+"""block_wise_kv_amd: the Fast-dLLM block-decoding hot path on MI355X.
+
+The compute runs in libfdllm.so (HIP kernels for gfx950, C ABI declared in
+include/fdllm.h); this package holds the ctypes binding and the build step.
+"""
+from .fdllm import (  # noqa: F401
+    BF16, F32, MODE, UNMASK_ADVANCE_BLOCK, FdllmError, SeqDesc, AttnDesc,
+    attn_desc, block_attn, block_attn_workspace, kv_refresh, lib, new_workspace,
+    seq_desc, unmask_threshold, unmask_workspace, version, workspace_init,
+)

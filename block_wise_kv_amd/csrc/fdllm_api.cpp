@@ -1,0 +1,364 @@
+// Host side of the libfdllm C ABI: argument validation, workspace sizing,
+// grid planning and kernel dispatch.  No call allocates, synchronises or
+// touches the HIP runtime before its arguments have been validated.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "fdllm.h"
+#include "fdllm_internal.h"
+
+using namespace fdllm;
+
+namespace {
+
+thread_local std::string g_err;
+
+fdllm_status fail(fdllm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+fdllm_status ok() {
+  g_err.clear();
+  return FDLLM_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validate the sequence descriptor; fills `sa` and the host bounds.
+fdllm_status check_seq(const fdllm_seq_desc* s, SeqArgs& sa, int& max_P) {
+  if (!s) return fail(FDLLM_ERR_INVALID_ARG, "seq descriptor is NULL");
+  if (s->batch < 1) return fail(FDLLM_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", s->batch);
+  if (s->gen_len < 1) return fail(FDLLM_ERR_INVALID_ARG, "gen_len must be >= 1 (got %d)", s->gen_len);
+  if (s->block_size < 1) return fail(FDLLM_ERR_INVALID_ARG, "block_size must be >= 1 (got %d)", s->block_size);
+  if (s->gen_len % s->block_size != 0)
+    return fail(FDLLM_ERR_INVALID_ARG, "gen_len %% block_size != 0 (%d %% %d)", s->gen_len, s->block_size);
+  if (s->max_seq_len < 1) return fail(FDLLM_ERR_INVALID_ARG, "max_seq_len must be >= 1");
+  if (s->prompt_lens) {
+    if (s->max_prompt_len < 0) return fail(FDLLM_ERR_INVALID_ARG, "max_prompt_len must be >= 0");
+    max_P = s->max_prompt_len;
+  } else {
+    if (s->prompt_len < 0) return fail(FDLLM_ERR_INVALID_ARG, "prompt_len must be >= 0");
+    max_P = s->prompt_len;
+  }
+  if ((int64_t)max_P + s->gen_len > s->max_seq_len)
+    return fail(FDLLM_ERR_INVALID_ARG, "prompt + gen_len (%lld) exceeds max_seq_len (%d)",
+                (long long)max_P + s->gen_len, s->max_seq_len);
+  const int nblocks = s->gen_len / s->block_size;
+  if (!s->block_idxs && (s->block_idx < 0 || s->block_idx >= nblocks))
+    return fail(FDLLM_ERR_INVALID_ARG, "block_idx %d outside [0, %d)", s->block_idx, nblocks);
+  sa.b = s->batch;
+  sa.Lcap = s->max_seq_len;
+  sa.G = s->gen_len;
+  sa.B = s->block_size;
+  sa.P = s->prompt_len;
+  sa.k = s->block_idx;
+  sa.plens = s->prompt_lens;
+  sa.bidx = s->block_idxs;
+  return FDLLM_OK;
+}
+
+fdllm_status check_attn_desc(const fdllm_attn_desc* d, bool need_q) {
+  if (!d) return fail(FDLLM_ERR_INVALID_ARG, "attn descriptor is NULL");
+  if (d->n_kv_heads < 1) return fail(FDLLM_ERR_INVALID_ARG, "n_kv_heads must be >= 1");
+  if (need_q) {
+    if (d->n_q_heads < 1) return fail(FDLLM_ERR_INVALID_ARG, "n_q_heads must be >= 1");
+    if (d->n_q_heads % d->n_kv_heads != 0)
+      return fail(FDLLM_ERR_INVALID_ARG, "n_q_heads %% n_kv_heads != 0 (%d, %d)", d->n_q_heads, d->n_kv_heads);
+    if (!(d->scale >= 0.f) || isinf(d->scale))
+      return fail(FDLLM_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 = 1/sqrt(d))");
+  }
+  if (d->dtype != FDLLM_BF16 && d->dtype != FDLLM_F32)
+    return fail(FDLLM_ERR_INVALID_ARG, "dtype %d is not a fdllm_dtype", d->dtype);
+  if (d->head_dim < 1) return fail(FDLLM_ERR_INVALID_ARG, "head_dim must be >= 1");
+  return FDLLM_OK;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int fresh_len_uniform(int mode, int P, int G, int B, int k) {
+  if (mode == FDLLM_CACHE_NONE) return P + G;
+  if (mode == FDLLM_CACHE_PREFIX) return G - k * B;
+  return B;
+}
+
+struct AttnSetup {
+  SeqArgs sa;
+  int max_P;
+  int nq_max;
+  int L_max;
+  AttnPlan plan;
+};
+
+fdllm_status setup_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* ad, int32_t mode, int32_t fresh_rows,
+                        AttnSetup& su) {
+  fdllm_status st = check_seq(seq, su.sa, su.max_P);
+  if (st) return st;
+  st = check_attn_desc(ad, true);
+  if (st) return st;
+  if (mode < FDLLM_CACHE_NONE || mode > FDLLM_CACHE_DUAL)
+    return fail(FDLLM_ERR_INVALID_ARG, "mode %d is not a fdllm_cache_mode", mode);
+  if (ad->dtype == FDLLM_BF16 && ad->head_dim != 128)
+    return fail(FDLLM_ERR_UNSUPPORTED, "bf16 attention supports head_dim 128 (got %d)", ad->head_dim);
+  if (ad->dtype == FDLLM_F32 && ad->head_dim != 64 && ad->head_dim != 128)
+    return fail(FDLLM_ERR_UNSUPPORTED, "f32 attention supports head_dim 64 or 128 (got %d)", ad->head_dim);
+  const bool ragged = seq->prompt_lens || seq->block_idxs;
+  int need;
+  if (!ragged) {
+    need = fresh_len_uniform(mode, seq->prompt_len, seq->gen_len, seq->block_size, seq->block_idx);
+  } else {
+    need = mode == FDLLM_CACHE_DUAL ? seq->block_size
+         : mode == FDLLM_CACHE_PREFIX ? seq->gen_len : su.max_P + seq->gen_len;
+  }
+  if (fresh_rows < need)
+    return fail(FDLLM_ERR_INVALID_ARG, "fresh_rows %d < %d rows needed by this mode/geometry", fresh_rows, need);
+  su.nq_max = need;
+  su.L_max = su.max_P + seq->gen_len;
+  const int64_t q_elems = (int64_t)seq->batch * fresh_rows * ad->n_q_heads * ad->head_dim;
+  const int64_t c_elems = (int64_t)seq->batch * ad->n_kv_heads * seq->max_seq_len * ad->head_dim;
+  if (q_elems >= ((int64_t)1 << 40) || c_elems >= ((int64_t)1 << 40))
+    return fail(FDLLM_ERR_INVALID_ARG, "tensor too large");
+  if ((int64_t)seq->batch * ad->n_q_heads * ((need + 31) / 32) * ((su.L_max + 127) / 128) >= ((int64_t)1 << 31))
+    return fail(FDLLM_ERR_INVALID_ARG, "grid too large");
+  su.plan = plan_block_attn(ad->dtype, seq->batch, ad->n_q_heads, ad->n_kv_heads, ad->head_dim, need, su.L_max);
+  return FDLLM_OK;
+}
+
+struct UnmaskSetup {
+  SeqArgs sa;
+  int max_P;
+  int chunk, nchunk;
+  size_t ws;
+};
+
+fdllm_status setup_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t dtype, UnmaskSetup& su) {
+  fdllm_status st = check_seq(seq, su.sa, su.max_P);
+  if (st) return st;
+  if (vocab < 1) return fail(FDLLM_ERR_INVALID_ARG, "vocab must be >= 1");
+  if (dtype != FDLLM_BF16 && dtype != FDLLM_F32) return fail(FDLLM_ERR_INVALID_ARG, "logits dtype %d invalid", dtype);
+  if (seq->block_size > 1024) return fail(FDLLM_ERR_UNSUPPORTED, "block_size > 1024");
+  if (seq->batch > 65535) return fail(FDLLM_ERR_UNSUPPORTED, "batch > 65535");
+  su.chunk = unmask_chunk_elems(dtype, vocab, seq->batch * seq->block_size);
+  su.nchunk = (vocab + su.chunk - 1) / su.chunk;
+  if ((int64_t)su.nchunk * seq->block_size >= ((int64_t)1 << 31) - 1)
+    return fail(FDLLM_ERR_INVALID_ARG, "vocab too large");
+  su.ws = unmask_workspace_bytes(seq->batch, seq->block_size, su.nchunk);
+  return FDLLM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fdllm_block_attn_workspace(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode,
+                                  int32_t fresh_rows) {
+  AttnSetup su;
+  if (setup_attn(seq, attn, mode, fresh_rows, su)) return 0;
+  return su.plan.ws_bytes;
+}
+
+fdllm_status fdllm_block_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode,
+                              int32_t fresh_rows, const void* q, const void* k_new, const void* v_new,
+                              const void* k_cache, const void* v_cache, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  AttnSetup su;
+  fdllm_status st = setup_attn(seq, attn, mode, fresh_rows, su);
+  if (st) return st;
+  if (!q || !k_new || !v_new || !out) return fail(FDLLM_ERR_INVALID_ARG, "q, k_new, v_new and out must be non-NULL");
+  if (mode != FDLLM_CACHE_NONE && (!k_cache || !v_cache))
+    return fail(FDLLM_ERR_INVALID_ARG, "k_cache and v_cache are required in PREFIX and DUAL modes");
+  const void* ptrs[] = {q, k_new, v_new, out, k_cache, v_cache};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(FDLLM_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const size_t es = attn->dtype == FDLLM_BF16 ? 2 : 4;
+  const size_t qb = (size_t)seq->batch * fresh_rows * attn->n_q_heads * attn->head_dim * es;
+  const size_t kvb = (size_t)seq->batch * fresh_rows * attn->n_kv_heads * attn->head_dim * es;
+  const size_t cb = (size_t)seq->batch * attn->n_kv_heads * seq->max_seq_len * attn->head_dim * es;
+  if (ranges_overlap(out, qb, q, qb) || ranges_overlap(out, qb, k_new, kvb) || ranges_overlap(out, qb, v_new, kvb) ||
+      (mode != FDLLM_CACHE_NONE && (ranges_overlap(out, qb, k_cache, cb) || ranges_overlap(out, qb, v_cache, cb))))
+    return fail(FDLLM_ERR_INVALID_ARG, "out must not alias an input");
+  if (su.plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < su.plan.ws_bytes)
+      return fail(FDLLM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", su.plan.ws_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(FDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  AttnArgs a{};
+  a.sq = su.sa;
+  a.mode = mode;
+  a.fresh_rows = fresh_rows;
+  a.Hq = attn->n_q_heads;
+  a.Hkv = attn->n_kv_heads;
+  a.g = a.Hq / a.Hkv;
+  a.scale = attn->scale > 0.f ? attn->scale : 1.0f / sqrtf((float)attn->head_dim);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.q = q;
+  a.kn = k_new;
+  a.vn = v_new;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.out = out;
+  a.n_qt = su.plan.n_qt;
+  a.n_split = su.plan.n_split;
+  a.kchunk = su.plan.kchunk;
+  a.n_items = su.plan.n_items;
+  a.per_xcd = su.plan.per_xcd;
+  if (su.plan.ws_bytes > 0) {
+    const size_t slots = (size_t)su.plan.n_items;
+    a.part = (float*)workspace;
+    a.cnt = (uint32_t*)((char*)workspace + slots * (size_t)(32 * 128 + 64) * sizeof(float));
+  }
+  hipError_t e = launch_block_attn(a, su.plan, attn->dtype, attn->head_dim, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "block_attn launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t fdllm_unmask_workspace(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype) {
+  UnmaskSetup su;
+  if (setup_unmask(seq, vocab, logits_dtype, su)) return 0;
+  return su.ws;
+}
+
+fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype,
+                                    const void* logits, int64_t seq_stride, int64_t row_stride, float threshold,
+                                    uint32_t flags, int32_t* tokens, uint8_t* mask, int32_t* n_decoded,
+                                    int32_t* decoded_pos, double* conf, int32_t* done_seqs, int32_t* n_done,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  UnmaskSetup su;
+  fdllm_status st = setup_unmask(seq, vocab, logits_dtype, su);
+  if (st) return st;
+  if (!logits || !tokens || !mask || !n_decoded)
+    return fail(FDLLM_ERR_INVALID_ARG, "logits, tokens, mask and n_decoded must be non-NULL");
+  if (isnan(threshold)) return fail(FDLLM_ERR_INVALID_ARG, "threshold is NaN");
+  if (flags & ~FDLLM_UNMASK_ADVANCE_BLOCK) return fail(FDLLM_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((flags & FDLLM_UNMASK_ADVANCE_BLOCK) && !seq->block_idxs)
+    return fail(FDLLM_ERR_INVALID_ARG, "FDLLM_UNMASK_ADVANCE_BLOCK needs a device block_idxs array");
+  if (row_stride < vocab) return fail(FDLLM_ERR_INVALID_ARG, "row_stride %lld < vocab %d", (long long)row_stride, vocab);
+  if (seq->batch > 1 && seq_stride < (int64_t)(seq->block_size - 1) * row_stride + vocab)
+    return fail(FDLLM_ERR_INVALID_ARG, "seq_stride %lld overlaps the rows of the previous sequence",
+                (long long)seq_stride);
+  if (!workspace || workspace_bytes < su.ws)
+    return fail(FDLLM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", su.ws,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(FDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const size_t es = logits_dtype == FDLLM_BF16 ? 2 : 4;
+  const bool vec = aligned16(logits) && ((size_t)row_stride * es) % 16 == 0 && ((size_t)seq_stride * es) % 16 == 0;
+  UnmaskArgs a{};
+  a.sq = su.sa;
+  a.V = vocab;
+  a.seq_stride = seq_stride;
+  a.row_stride = row_stride;
+  a.logits = logits;
+  a.tau = threshold;
+  a.flags = flags;
+  a.tokens = tokens;
+  a.mask = mask;
+  a.n_decoded = n_decoded;
+  a.decoded_pos = decoded_pos;
+  a.conf = conf;
+  a.done_seqs = done_seqs;
+  a.n_done = n_done;
+  a.nchunk = su.nchunk;
+  a.chunk = su.chunk;
+  char* w = (char*)workspace;
+  a.part = (UnmaskPartial*)w;
+  w += (size_t)seq->batch * seq->block_size * su.nchunk * sizeof(UnmaskPartial);
+  a.seq_cnt = (uint32_t*)w;
+  w += (size_t)seq->batch * 4;
+  a.glob_cnt = (uint32_t*)w;
+  w += 16;
+  a.done_flag = (int32_t*)w;
+  hipError_t e = launch_unmask(a, logits_dtype, vec, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "unmask launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fdllm_status fdllm_kv_refresh(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode,
+                              const void* k_src, const void* v_src, void* k_cache, void* v_cache,
+                              const int32_t* seq_ids, const int32_t* n_seq, void* stream) {
+  SeqArgs sa;
+  int max_P;
+  fdllm_status st = check_seq(seq, sa, max_P);
+  if (st) return st;
+  st = check_attn_desc(attn, false);
+  if (st) return st;
+  if (mode < FDLLM_CACHE_NONE || mode > FDLLM_CACHE_DUAL)
+    return fail(FDLLM_ERR_INVALID_ARG, "mode %d is not a fdllm_cache_mode", mode);
+  if (seq_ids && !n_seq) return fail(FDLLM_ERR_INVALID_ARG, "seq_ids needs the device count n_seq");
+  if (mode == FDLLM_CACHE_NONE) return ok();  // nothing is cached
+  if (!k_src || !v_src || !k_cache || !v_cache)
+    return fail(FDLLM_ERR_INVALID_ARG, "k_src, v_src, k_cache and v_cache must be non-NULL");
+  const void* ptrs[] = {k_src, v_src, k_cache, v_cache};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(FDLLM_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t es = attn->dtype == FDLLM_BF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)attn->head_dim * es;
+  if (row_bytes % 16 != 0) return fail(FDLLM_ERR_UNSUPPORTED, "head_dim * element size must be a multiple of 16");
+  size_t vpr = row_bytes / 16;
+  int shift = 0;
+  while ((1u << shift) < vpr) ++shift;
+  if ((1u << shift) != vpr) return fail(FDLLM_ERR_UNSUPPORTED, "head_dim * element size / 16 must be a power of two");
+  if ((((int64_t)seq->max_seq_len * attn->n_kv_heads) << shift) >= ((int64_t)1 << 31))
+    return fail(FDLLM_ERR_INVALID_ARG, "per-sequence cache too large");
+  const size_t cb = (size_t)seq->batch * attn->n_kv_heads * seq->max_seq_len * row_bytes;
+  if (ranges_overlap(k_cache, cb, k_src, cb) || ranges_overlap(k_cache, cb, v_src, cb) ||
+      ranges_overlap(v_cache, cb, k_src, cb) || ranges_overlap(v_cache, cb, v_src, cb) ||
+      ranges_overlap(k_cache, cb, v_cache, cb))
+    return fail(FDLLM_ERR_INVALID_ARG, "caches must not alias the sources or each other");
+  RefreshArgs a{};
+  a.sq = sa;
+  a.mode = mode;
+  a.Hkv = attn->n_kv_heads;
+  a.row_vec_shift = shift;
+  a.hkv_div = make_fastdiv((uint32_t)attn->n_kv_heads);
+  a.k_src = (const uint4*)k_src;
+  a.v_src = (const uint4*)v_src;
+  a.k_cache = (uint4*)k_cache;
+  a.v_cache = (uint4*)v_cache;
+  a.seq_ids = seq_ids;
+  a.n_seq = n_seq;
+  const int max_rows = max_P + seq->gen_len;
+  hipError_t e = launch_kv_refresh(a, max_rows, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "kv_refresh launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fdllm_status fdllm_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (bytes == 0) return ok();
+  if (!workspace) return fail(FDLLM_ERR_INVALID_ARG, "workspace is NULL");
+  if (bytes % 4 != 0 || !aligned16(workspace))
+    return fail(FDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned and a multiple of 4 bytes");
+  hipError_t e = launch_fill_zero(workspace, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "fill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* fdllm_status_string(int32_t status) {
+  switch (status) {
+    case FDLLM_OK: return "FDLLM_OK";
+    case FDLLM_ERR_INVALID_ARG: return "FDLLM_ERR_INVALID_ARG";
+    case FDLLM_ERR_UNSUPPORTED: return "FDLLM_ERR_UNSUPPORTED";
+    case FDLLM_ERR_WORKSPACE: return "FDLLM_ERR_WORKSPACE";
+    case FDLLM_ERR_LAUNCH: return "FDLLM_ERR_LAUNCH";
+    default: return "FDLLM_ERR_UNKNOWN";
+  }
+}
+
+const char* fdllm_last_error(void) { return g_err.c_str(); }
+
+int32_t fdllm_version(void) { return FDLLM_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of libfdllm.  Not installed; the public ABI is include/fdllm.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fdllm {
+
+// Division by a run-time invariant divisor with one multiply-high and a
+// shift (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994).  Valid for 0 <= n < 2^31 and 1 <= d < 2^31.
+struct FastDiv {
+  uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.s = s;
+  // m = floor(2^32 * (2^s - d) / d) + 1
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  uint32_t t = __umulhi(n, f.m);
+  return (t + n) >> f.s;
+}
+
+// Sequence geometry resolved for the device.
+struct SeqArgs {
+  int b, Lcap, G, B;
+  int P, k;                 // uniform values when the pointers are null
+  const int32_t* plens;     // [b] or null
+  int32_t* bidx;            // [b] or null
+};
+
+__device__ __forceinline__ int seq_prompt(const SeqArgs& s, int i) { return s.plens ? s.plens[i] : s.P; }
+__device__ __forceinline__ int seq_block(const SeqArgs& s, int i) { return s.bidx ? s.bidx[i] : s.k; }
+
+enum { MODE_NONE = 0, MODE_PREFIX = 1, MODE_DUAL = 2 };
+
+// ------------------------------------------------------------------ refresh
+struct RefreshArgs {
+  SeqArgs sq;
+  int mode;
+  int Hkv;
+  int row_vec_shift;        // log2(16-byte vectors per (row, head))
+  FastDiv hkv_div;
+  const uint4* k_src;
+  const uint4* v_src;
+  uint4* k_cache;
+  uint4* v_cache;
+  const int32_t* seq_ids;   // null = all
+  const int32_t* n_seq;
+};
+hipError_t launch_kv_refresh(const RefreshArgs& a, int max_rows, hipStream_t st);
+
+// ------------------------------------------------------------------ unmask
+struct UnmaskPartial {      // per (sequence, row, vocab chunk)
+  float m;                  // max logit of the chunk
+  int32_t idx;              // lowest vocab id attaining m in the chunk
+  double z;                 // sum over the chunk of exp(logit - m)
+};
+
+struct UnmaskArgs {
+  SeqArgs sq;
+  int V;
+  int64_t seq_stride, row_stride;  // elements
+  const void* logits;
+  float tau;
+  uint32_t flags;
+  int32_t* tokens;
+  uint8_t* mask;
+  int32_t* n_decoded;
+  int32_t* decoded_pos;
+  double* conf;
+  int32_t* done_seqs;
+  int32_t* n_done;
+  UnmaskPartial* part;      // [b][B][nchunk]
+  uint32_t* seq_cnt;        // [b]
+  uint32_t* glob_cnt;       // [1]
+  int32_t* done_flag;       // [b]
+  int nchunk;
+  int chunk;                // vocab entries per chunk
+};
+size_t unmask_workspace_bytes(int b, int B, int nchunk);
+int unmask_chunk_elems(int dtype, int V, int rows);
+hipError_t launch_unmask(const UnmaskArgs& a, int dtype, bool vec, hipStream_t st);
+
+// ------------------------------------------------------------------ attention
+struct AttnArgs {
+  SeqArgs sq;
+  int mode;
+  int fresh_rows;
+  int Hq, Hkv, g;
+  float scale;              // softmax scale
+  float scale_log2;         // scale * log2(e)
+  const void* q;
+  const void* kn;
+  const void* vn;
+  const void* kc;
+  const void* vc;
+  void* out;
+  float* part;              // split-key partials (null when n_split == 1)
+  uint32_t* cnt;            // split-key counters [b][Hq][n_qt]
+  int n_qt;                 // query tiles per (sequence, head)
+  int n_split;              // key chunks per (sequence, head, query tile)
+  int kchunk;               // keys per chunk
+  int n_items;
+  int per_xcd;              // work items per XCD slice of the grid
+};
+
+struct AttnPlan {
+  int n_qt, n_split, kchunk, n_items, per_xcd, grid;
+  size_t ws_bytes;
+};
+AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max);
+hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, int d, hipStream_t st);
+
+// ------------------------------------------------------------------ misc
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace fdllm

@@ -1,0 +1,202 @@
+/*
+ * fdllm.h -- C ABI of libfdllm, the per-step hot path of Fast-dLLM
+ * block-wise masked-diffusion decoding on AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what each call computes:
+ *   [ABS]    Fast-dLLM: Training-free Acceleration of Diffusion LLM by
+ *            Enabling KV Cache and Parallel Decoding, paper summary page
+ *            (arXiv 2505.22618v3), "Abstract" and method notes.
+ *   [NEWS]   aibase news article on Fast-dLLM, "Innovations in the Fast-dLLM
+ *            Framework" items 1-2, "The Challenges and Opportunities".
+ *   [README] Fast-dLLM project README mirror, "Key techniques" items 1-2 and
+ *            "Usage" (flags --gen_length, --block_size, --use_cache,
+ *            --if_cache_position, --threshold).
+ *   [REV]    ICLR reviews of Fast-dLLM, review 4 (refresh after each block).
+ *
+ * Conventions (all calls):
+ *   - Pointers are DEVICE pointers unless marked "host".  Descriptors are
+ *     host structs read during the call only.
+ *   - The caller owns every buffer.  The library never allocates device
+ *     memory and never synchronises; every call is asynchronous and ordered
+ *     on `stream` (a hipStream_t passed as void*, NULL = default stream).
+ *   - Host-side scalars and pointers are validated before any launch; on
+ *     failure nothing is launched, an FDLLM_ERR_* code is returned and
+ *     fdllm_last_error() describes it.  Device-resident per-sequence arrays
+ *     (prompt_lens, block_idxs, seq_ids, n_seq) are trusted.
+ *   - No exception or abort crosses the ABI.  Thread-safe: no global
+ *     device state; fdllm_last_error() is per host thread.
+ *   - Workspaces hold self-resetting counters: zero a workspace once with
+ *     fdllm_workspace_init after allocating it; every call leaves its
+ *     counters at zero again.  Two calls that share a workspace must not
+ *     run concurrently (same stream, or ordered streams).
+ *
+ * Notation: batch b; sequence i has prompt length P_i, shared gen length G,
+ * L_i = P_i + G; block size B (G % B == 0); block index k_i in [0, G/B);
+ * block k covers positions [P_i + k*B, P_i + (k+1)*B).  Hq query heads,
+ * Hkv key/value heads (Hq % Hkv == 0, query head h reads KV head
+ * h / (Hq/Hkv)), head dim d.  Lcap = row capacity of tokens, mask and caches.
+ */
+#ifndef FDLLM_H
+#define FDLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FDLLM_VERSION 100 /* 1.0.0 */
+
+typedef enum {
+  FDLLM_OK = 0,
+  FDLLM_ERR_INVALID_ARG = 1, /* a scalar, pointer or size is invalid */
+  FDLLM_ERR_UNSUPPORTED = 2, /* valid, but not implemented (dtype, head_dim, alignment) */
+  FDLLM_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace query */
+  FDLLM_ERR_LAUNCH = 4       /* the HIP runtime rejected a kernel launch */
+} fdllm_status;
+
+/* Which K/V rows are recomputed ("fresh") this step; all others are read
+ * from the cache.  [NEWS] item 1, [README] item 1 and its Usage flags:
+ *   NONE   (no cache)                       fresh rows [0, L_i)
+ *   PREFIX (--use_cache)                    fresh rows [P_i + k_i*B, L_i)
+ *   DUAL   (--use_cache --if_cache_position) fresh rows [P_i + k_i*B, P_i + (k_i+1)*B)
+ * The fresh rows are also the query rows: nq_i = a1 - a0. */
+typedef enum { FDLLM_CACHE_NONE = 0, FDLLM_CACHE_PREFIX = 1, FDLLM_CACHE_DUAL = 2 } fdllm_cache_mode;
+
+typedef enum { FDLLM_BF16 = 0, FDLLM_F32 = 1 } fdllm_dtype;
+
+/* Per-batch sequence geometry (host struct). */
+typedef struct {
+  int32_t batch;            /* b >= 1 */
+  int32_t max_seq_len;      /* Lcap >= every L_i */
+  int32_t gen_len;          /* G >= 1, G % block_size == 0 */
+  int32_t block_size;       /* B >= 1 */
+  int32_t prompt_len;       /* uniform P, used when prompt_lens == NULL */
+  int32_t block_idx;        /* uniform k, used when block_idxs == NULL; 0 <= k < G/B */
+  const int32_t* prompt_lens; /* device [b] or NULL (then every P_i = prompt_len) */
+  int32_t* block_idxs;      /* device [b] or NULL (then every k_i = block_idx);
+                               fdllm_unmask_threshold may advance it */
+  int32_t max_prompt_len;   /* host upper bound of prompt_lens (used only when
+                               prompt_lens != NULL, for grid sizing);
+                               max_prompt_len + G <= Lcap */
+} fdllm_seq_desc;
+
+/* Attention geometry (host struct). */
+typedef struct {
+  int32_t n_q_heads;   /* Hq >= 1 */
+  int32_t n_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;    /* d: 128 for bf16; 64 or 128 for f32 */
+  int32_t dtype;       /* fdllm_dtype of q, k, v, caches and out */
+  float scale;         /* softmax scale; 0 selects 1/sqrt(d) */
+} fdllm_attn_desc;
+
+/* ------------------------------------------------------------------ */
+/* (a) block attention                                                 */
+/* ------------------------------------------------------------------ */
+
+/* Bytes of workspace fdllm_block_attn needs for this geometry (0 when the
+ * key range is not split across workgroups).  Returns 0 on invalid input. */
+size_t fdllm_block_attn_workspace(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn,
+                                  int32_t mode, int32_t fresh_rows);
+
+/* Bidirectional attention of the fresh rows of each sequence over the key
+ * rows [0, L_i), with K/V row j taken from k_new/v_new when a0 <= j < a1
+ * and from the cache otherwise ([README] item 1, [NEWS] "Challenges": no
+ * causal mask).  out[r] = sum_j softmax_j(scale * q[r].K_j) V_j.
+ *
+ *   q       [b][fresh_rows][Hq][d]   row r holds position a0 + r
+ *   k_new   [b][fresh_rows][Hkv][d]  fresh K rows, same row convention
+ *   v_new   [b][fresh_rows][Hkv][d]
+ *   k_cache [b][Hkv][Lcap][d]        head-major cache; NULL allowed in NONE
+ *   v_cache [b][Hkv][Lcap][d]
+ *   out     [b][fresh_rows][Hq][d]   same dtype as the inputs; rows >= nq_i
+ *                                    are not written; must not alias inputs
+ * fresh_rows: row capacity per sequence of the fresh tensors; must be
+ * >= nq_i for every sequence (checked on the host for uniform batches; for
+ * ragged batches it must be >= B (DUAL), G (PREFIX), max_prompt_len + G
+ * (NONE)).  All tensors contiguous; base pointers 16-byte aligned. */
+fdllm_status fdllm_block_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn,
+                              int32_t mode, int32_t fresh_rows,
+                              const void* q, const void* k_new, const void* v_new,
+                              const void* k_cache, const void* v_cache, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* (b) confidence-aware parallel unmasking                            */
+/* ------------------------------------------------------------------ */
+
+#define FDLLM_UNMASK_ADVANCE_BLOCK 1u /* k_i += 1 when block i is done and k_i + 1 < G/B
+                                         (needs seq->block_idxs != NULL) */
+
+size_t fdllm_unmask_workspace(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype);
+
+/* One decoding step of the threshold rule ([README] item 2, [NEWS] item 2,
+ * [ABS]).  For every masked position of the current block (row t <->
+ * position P_i + k_i*B + t):
+ *   m_t = max_v logit, Z_t = sum_v exp(logit - m_t), conf_t = 1 / Z_t,
+ *   tok_t = lowest v with logit == m_t.
+ * Selected set S_i = { t masked : conf_t > threshold } (strict, compared in
+ * float64); if S_i is empty and some row is masked, S_i = { the masked row
+ * with the largest conf_t, lowest t on a tie }.  For t in S_i:
+ * tokens[pos] = tok_t, mask[pos] = 0.  Decoded tokens are never re-masked.
+ *
+ *   logits     [b][B][vocab] addressed as logits + i*seq_stride + t*row_stride
+ *              (strides in elements); rows of unmasked positions are not read.
+ *              bf16 or f32; every logit must be finite.
+ *   tokens     int32 [b][Lcap] in/out;  mask uint8 [b][Lcap] in/out (1 = masked)
+ *   n_decoded  int32 [b] out: |S_i|
+ *   decoded_pos int32 [b][B] out or NULL: S_i ascending, padded with -1
+ *   conf       double [b][B] out or NULL: conf_t for masked rows, NaN otherwise
+ *   done_seqs  int32 [b] out or NULL: ascending ids of sequences whose block
+ *              has no masked position left after this step
+ *   n_done     int32 [1] out or NULL: number of entries in done_seqs
+ * threshold: any finite float (>= 1 always falls back to one token; <= 0
+ * decodes every masked row); NaN is rejected.
+ * Vector path: logits, seq_stride and row_stride 16-byte aligned (in bytes);
+ * otherwise a scalar path is used. */
+fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype,
+                                    const void* logits, int64_t seq_stride, int64_t row_stride,
+                                    float threshold, uint32_t flags,
+                                    int32_t* tokens, uint8_t* mask, int32_t* n_decoded,
+                                    int32_t* decoded_pos, double* conf,
+                                    int32_t* done_seqs, int32_t* n_done,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* (c) KV-cache refresh at a block boundary                           */
+/* ------------------------------------------------------------------ */
+
+/* Copy the K/V of a full forward into the caches ([REV] review 4, [NEWS]
+ * item 1): cache[i][h][j][:] = src[i][j][h][:] for j < L_i (DUAL),
+ * j < P_i + k_i*B (PREFIX, with the block index of the block about to be
+ * decoded), nothing (NONE).  Other rows are untouched.  Bit-exact copy.
+ *
+ *   k_src, v_src     [b][Lcap][Hkv][d] token-major
+ *   k_cache, v_cache [b][Hkv][Lcap][d] head-major
+ *   seq_ids  int32 device list of sequences to refresh, or NULL for all b
+ *   n_seq    int32 device [1]: entries of seq_ids (required with seq_ids),
+ *            e.g. the done_seqs / n_done outputs of fdllm_unmask_threshold.
+ * Uses attn->n_kv_heads, head_dim and dtype; n_q_heads and scale are ignored.
+ * Pointers 16-byte aligned. */
+fdllm_status fdllm_kv_refresh(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode,
+                              const void* k_src, const void* v_src, void* k_cache, void* v_cache,
+                              const int32_t* seq_ids, const int32_t* n_seq, void* stream);
+
+/* ------------------------------------------------------------------ */
+/* utilities                                                           */
+/* ------------------------------------------------------------------ */
+
+/* Zero a workspace (a fill kernel on `stream`; no memset node, so it can be
+ * captured in a graph).  bytes must be a multiple of 4. */
+fdllm_status fdllm_workspace_init(void* workspace, size_t bytes, void* stream);
+
+const char* fdllm_status_string(int32_t status);
+const char* fdllm_last_error(void);
+int32_t fdllm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FDLLM_H */

@@ -1,0 +1,155 @@
+"""libfdllm loads, exports every symbol of include/fdllm.h, and rejects
+invalid arguments on the host before any launch (CPU only: every call here
+fails validation, so no kernel is launched and no device is touched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_wise_kv_amd as fd
+from block_wise_kv_amd import fdllm as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fdllm.h")
+
+# fake, 16-byte aligned, never dereferenced device pointers
+P1, P2, P3, P4, P5, P6, P7 = ((n + 1) << 36 for n in range(7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fdllm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("fdllm_block_attn", "fdllm_unmask_threshold", "fdllm_kv_refresh"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fd.lib()
+    names = declared_functions()
+    assert len(names) >= 9
+    out = subprocess.run(["nm", "-D", "--defined-only", F.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, f"{n} not exported"
+        assert hasattr(lib, n)
+    # the binding declares the same set
+    assert {s[0] for s in F._SIGS} == set(names)
+
+
+def test_version_and_strings():
+    L = fd.lib()
+    assert fd.version() == 100
+    assert L.fdllm_status_string(1) == b"FDLLM_ERR_INVALID_ARG"
+    assert L.fdllm_status_string(77) == b"FDLLM_ERR_UNKNOWN"
+
+
+def _seq(**kw):
+    base = dict(batch=1, max_seq_len=768, gen_len=256, block_size=32, prompt_len=512, block_idx=0)
+    base.update(kw)
+    return F.seq_desc(**base)
+
+
+def _attn_call(seq, ad, mode=2, fresh_rows=32, q=P1, kn=P2, vn=P3, kc=P4, vc=P5, out=P6, ws=None, wsb=0):
+    L = fd.lib()
+    st = L.fdllm_block_attn(ctypes.byref(seq), ctypes.byref(ad), mode, fresh_rows, q, kn, vn, kc, vc, out,
+                            ws, wsb, None)
+    return st, L.fdllm_last_error().decode()
+
+
+BF = F.attn_desc(32, 32, 128, F.BF16)
+
+
+@pytest.mark.parametrize("case, seq, ad, kw, status, msg", [
+    ("batch0", _seq(batch=0), BF, {}, 1, "batch"),
+    ("gen%block", _seq(gen_len=250), BF, {}, 1, "gen_len"),
+    ("block_idx", _seq(block_idx=8), BF, {}, 1, "block_idx"),
+    ("L>Lcap", _seq(max_seq_len=700), BF, {}, 1, "max_seq_len"),
+    ("gqa", _seq(), F.attn_desc(28, 5, 128, F.BF16), {}, 1, "n_kv_heads"),
+    ("bf16 d64", _seq(), F.attn_desc(32, 32, 64, F.BF16), {}, 2, "head_dim"),
+    ("f32 d96", _seq(), F.attn_desc(32, 32, 96, F.F32), {}, 2, "head_dim"),
+    ("dtype", _seq(), F.attn_desc(32, 32, 128, 7), {}, 1, "dtype"),
+    ("mode", _seq(), BF, {"mode": 3}, 1, "mode"),
+    ("nan scale", _seq(), F.attn_desc(32, 32, 128, F.BF16, float("nan")), {}, 1, "scale"),
+    ("no cache", _seq(), BF, {"kc": None}, 1, "cache"),
+    ("fresh_rows", _seq(), BF, {"fresh_rows": 31}, 1, "fresh_rows"),
+    ("prefix rows", _seq(block_idx=2), BF, {"mode": 1, "fresh_rows": 100}, 1, "fresh_rows"),
+    ("align", _seq(), BF, {"q": P1 + 2}, 1, "aligned"),
+    ("alias", _seq(), BF, {"out": P1}, 1, "alias"),
+    ("null q", _seq(), BF, {"q": None}, 1, "non-NULL"),
+    ("workspace", _seq(), BF, {}, 3, "workspace"),
+])
+def test_block_attn_rejects(case, seq, ad, kw, status, msg):
+    st, err = _attn_call(seq, ad, **kw)
+    assert st == status, (case, st, err)
+    assert msg in err
+
+
+def test_attn_workspace_query():
+    # LLaDA-8B shape at batch 1 splits the 768 keys over several workgroups
+    n = F.block_attn_workspace(_seq(), BF, "dual", 32)
+    assert n > 0 and n % 256 == 0
+    assert F.block_attn_workspace(_seq(batch=0), BF, "dual", 32) == 0
+    # f32 path never needs one
+    assert F.block_attn_workspace(_seq(), F.attn_desc(32, 32, 128, F.F32), "dual", 32) == 0
+
+
+def _unmask_call(seq, vocab=126464, dt=F.BF16, logits=P1, ss=None, rs=None, tau=0.9, flags=0, ws=P7,
+                 wsb=1 << 30):
+    L = fd.lib()
+    rs = vocab if rs is None else rs
+    ss = seq.block_size * rs if ss is None else ss
+    st = L.fdllm_unmask_threshold(ctypes.byref(seq), vocab, dt, logits, ss, rs, tau, flags, P2, P3, P4, P5, P6,
+                                  None, None, ws, wsb, None)
+    return st, L.fdllm_last_error().decode()
+
+
+@pytest.mark.parametrize("case, seq, kw, status, msg", [
+    ("nan tau", _seq(), {"tau": float("nan")}, 1, "NaN"),
+    ("vocab", _seq(), {"vocab": 0}, 1, "vocab"),
+    ("dtype", _seq(), {"dt": 5}, 1, "dtype"),
+    ("flags", _seq(), {"flags": 2}, 1, "flags"),
+    ("advance", _seq(), {"flags": 1}, 1, "block_idxs"),
+    ("row stride", _seq(), {"rs": 100}, 1, "row_stride"),
+    ("seq stride", _seq(batch=2), {"ss": 126464}, 1, "seq_stride"),
+    ("no ws", _seq(), {"ws": None, "wsb": 0}, 3, "workspace"),
+    ("small ws", _seq(), {"wsb": 64}, 3, "workspace"),
+    ("big block", _seq(gen_len=2048, block_size=2048, max_seq_len=4096), {}, 2, "block_size"),
+])
+def test_unmask_rejects(case, seq, kw, status, msg):
+    st, err = _unmask_call(seq, **kw)
+    assert st == status, (case, st, err)
+    assert msg in err
+
+
+def test_unmask_workspace_query():
+    n = F.unmask_workspace(_seq(), 126464, F.BF16)
+    assert n > 0 and n % 256 == 0
+    assert F.unmask_workspace(_seq(), 0, F.BF16) == 0
+
+
+def test_refresh_rejects_and_none_is_noop():
+    L = fd.lib()
+    ad = F.attn_desc(0, 32, 128, F.BF16)
+    st = L.fdllm_kv_refresh(ctypes.byref(_seq()), ctypes.byref(ad), 2, P1, P2, P3, P4, P5, None, None)
+    assert st == 1 and "n_seq" in L.fdllm_last_error().decode()
+    st = L.fdllm_kv_refresh(ctypes.byref(_seq()), ctypes.byref(ad), 2, P1, P2, P1, P4, None, None, None)
+    assert st == 1 and "alias" in L.fdllm_last_error().decode()
+    st = L.fdllm_kv_refresh(ctypes.byref(_seq()), ctypes.byref(ad), 2, None, P2, P3, P4, None, None, None)
+    assert st == 1
+    # no-cache mode keeps nothing: OK without touching any pointer
+    st = L.fdllm_kv_refresh(ctypes.byref(_seq()), ctypes.byref(ad), 0, None, None, None, None, None, None, None)
+    assert st == 0
+
+
+def test_workspace_init_rejects():
+    L = fd.lib()
+    assert L.fdllm_workspace_init(None, 64, None) == 1
+    assert L.fdllm_workspace_init(P1 + 4, 64, None) == 1
+    assert L.fdllm_workspace_init(P1, 0, None) == 0

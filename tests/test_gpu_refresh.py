@@ -1,0 +1,164 @@
+"""GPU parity: fdllm_kv_refresh against the oracle (bit-exact), and the
+full ragged step (28 x attention, one unmask, refresh of the finished
+sequences' 28 layer caches)."""
+import numpy as np
+import pytest
+import torch
+
+import block_wise_kv_amd as fd
+from gpu_util import (DEV, check_attn, compare_unmask, oracle_attn_subset, require_gpu, run_attn, say,
+                      seq_for, to_dev)
+from oracle import attn_ref, refresh_ref, unmask_ref
+from workloads import (AttnInputs, make_attn_inputs, make_decode_state, make_logits, make_refresh_src,
+                       n_masked_c5, shape_c1, shape_c3, shape_c5, shape_custom)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _sentinel(s, dt):
+    shp = (s.batch, s.n_kv_heads, s.max_seq_len, s.head_dim)
+    return np.full(shp, -3.0, np.float32), np.full(shp, 5.0, np.float32)
+
+
+def _run_refresh(s, mode, ks, vs, kc0, vc0, ragged, seq_ids=None):
+    keep = []
+    seq = seq_for(s, ragged, keep)
+    k_src, v_src = to_dev(ks, s.dtype), to_dev(vs, s.dtype)
+    kc, vc = to_dev(kc0, s.dtype), to_dev(vc0, s.dtype)
+    ids = n = None
+    if seq_ids is not None:
+        ids = torch.tensor(list(seq_ids) + [0] * (s.batch - len(seq_ids)), dtype=torch.int32, device=DEV)
+        n = torch.tensor([len(seq_ids)], dtype=torch.int32, device=DEV)
+    fd.kv_refresh(seq, mode, k_src, v_src, kc, vc, ids, n)
+    torch.cuda.synchronize()
+    return kc.float().cpu().numpy(), vc.float().cpu().numpy()
+
+
+CASES = [
+    ("c1", shape_c1(), False),
+    ("ragged_bf16", shape_custom("rr", "bf16", 3, 4, 2, 128, [37, 100, 5], 96, 32, [0, 2, 1], 64, cfg_id=70), True),
+    ("f32_d64", shape_custom("rf", "f32", 2, 4, 3, 64, [12, 4], 32, 8, [1, 3], 64, cfg_id=71), True),
+]
+
+
+@pytest.mark.parametrize("mode", ["dual", "prefix", "none"])
+@pytest.mark.parametrize("name,s,ragged", CASES, ids=[c[0] for c in CASES])
+def test_refresh_modes(name, s, ragged, mode):
+    ks, vs = make_refresh_src(s)
+    kc0, vc0 = _sentinel(s, s.dtype)
+    say(f"refresh {name} {mode}")
+    kc, vc = _run_refresh(s, mode, ks, vs, kc0, vc0, ragged)
+    rk, rv = refresh_ref(ks, vs, kc0, vc0, s.prompt_lens, s.gen_len, s.block_size, s.block_idxs, mode)
+    assert np.array_equal(kc, rk) and np.array_equal(vc, rv)
+
+
+def test_refresh_subset_from_device_list():
+    s = shape_custom("rs", "bf16", 5, 4, 2, 128, [10, 20, 30, 40, 50], 64, 16, [0, 1, 2, 3, 0], 64, cfg_id=72)
+    ks, vs = make_refresh_src(s)
+    kc0, vc0 = _sentinel(s, s.dtype)
+    say("refresh subset")
+    kc, vc = _run_refresh(s, "dual", ks, vs, kc0, vc0, True, seq_ids=[4, 1])
+    rk, rv = refresh_ref(ks, vs, kc0, vc0, s.prompt_lens, s.gen_len, s.block_size, s.block_idxs, "dual",
+                         seq_ids=[4, 1])
+    assert np.array_equal(kc, rk) and np.array_equal(vc, rv)
+
+
+def test_c3_refresh_every_block_boundary():
+    # Dream-7B shape: prefix-mode refresh at each of the 32 block boundaries
+    # (rows [0, P + kB)) and the DualCache refresh (rows [0, L)).
+    base = shape_c3(0)
+    ks, vs = make_refresh_src(base)
+    k_src, v_src = to_dev(ks, "bf16"), to_dev(vs, "bf16")
+    kc0, vc0 = _sentinel(base, "bf16")
+    kc, vc = to_dev(kc0, "bf16"), to_dev(vc0, "bf16")
+    ks_t = torch.from_numpy(ks).to(DEV).to(torch.bfloat16)
+    for k in range(32):
+        s = shape_c3(k)
+        say(f"c3 refresh prefix k={k}")
+        fd.kv_refresh(seq_for(s), "prefix", k_src, v_src, kc, vc)
+        torch.cuda.synchronize()
+        hi = 1024 + 32 * k
+        # rows below hi equal the source, the rest keep the sentinel (checked on the device)
+        assert torch.equal(kc[:, :, :hi], ks_t[:, :hi].transpose(1, 2))
+        assert bool((kc[:, :, hi:] == -3.0).all())
+    # exact check against the oracle for the final state
+    rk, rv = refresh_ref(ks, vs, kc0, vc0, base.prompt_lens, base.gen_len, base.block_size,
+                         np.full(8, 31, np.int32), "prefix")
+    assert np.array_equal(kc.float().cpu().numpy(), rk) and np.array_equal(vc.float().cpu().numpy(), rv)
+    fd.kv_refresh(seq_for(base), "dual", k_src, v_src, kc, vc)
+    torch.cuda.synchronize()
+    rk, rv = refresh_ref(ks, vs, kc0, vc0, base.prompt_lens, base.gen_len, base.block_size, base.block_idxs,
+                         "dual")
+    assert np.array_equal(kc.float().cpu().numpy(), rk) and np.array_equal(vc.float().cpu().numpy(), rv)
+
+
+def test_c5_full_step_28_layers():
+    """Ragged Dream-7B batch: 28 x block attention (one cache per layer), one
+    unmask with block advance, then refresh of every finished sequence's 28
+    layer caches from the device-side done list."""
+    s = shape_c5()
+    n_layers = 28
+    keep = []
+    bidx = torch.from_numpy(s.block_idxs.astype(np.int32)).to(DEV)
+    seq = seq_for(s, True, keep, bidx)
+    inp = make_attn_inputs(s, "dual")
+    q, kn, vn = to_dev(inp.q, "bf16"), to_dev(inp.k_new, "bf16"), to_dev(inp.v_new, "bf16")
+    kc0, vc0 = to_dev(inp.k_cache, "bf16"), to_dev(inp.v_cache, "bf16")
+    # each layer owns its cache; layer l holds the same values scaled by a
+    # power of two (exact in bf16), so every layer's output is distinct
+    kcs = [kc0 * (2.0 ** -(l % 3)) for l in range(n_layers)]
+    vcs = [vc0 for _ in range(n_layers)]
+    ad = fd.attn_desc(28, 4, 128, fd.BF16)
+    ws = fd.new_workspace(fd.block_attn_workspace(seq, ad, "dual", q.shape[1]))
+    outs = [torch.empty_like(q) for _ in range(n_layers)]
+    logits = make_logits(s, "calibrated")
+    tokens, mask = make_decode_state(s, n_masked_c5(s))
+    lg = to_dev(logits, "bf16")
+    tk = torch.from_numpy(tokens).to(DEV)
+    mk = torch.from_numpy(mask).to(DEV)
+    nd = torch.zeros(s.batch, dtype=torch.int32, device=DEV)
+    dp = torch.zeros((s.batch, 32), dtype=torch.int32, device=DEV)
+    ds = torch.zeros(s.batch, dtype=torch.int32, device=DEV)
+    nn = torch.zeros(1, dtype=torch.int32, device=DEV)
+    uws = fd.new_workspace(fd.unmask_workspace(seq, s.vocab, fd.BF16))
+    srcs = make_refresh_src(s)
+    k_src, v_src = to_dev(srcs[0], "bf16"), to_dev(srcs[1], "bf16")
+    say("c5 full step: 28 x attn + unmask + 28 x refresh(done)")
+    for l in range(n_layers):
+        fd.block_attn(seq, "dual", q, kn, vn, kcs[l], vcs[l], outs[l], ws)
+    fd.unmask_threshold(seq, lg, 0.7, tk, mk, nd, dp, None, ds, nn, uws, flags=fd.UNMASK_ADVANCE_BLOCK)
+    for l in range(n_layers):
+        fd.kv_refresh(seq, "dual", k_src, v_src, kcs[l], vcs[l], ds, nn)
+    torch.cuda.synchronize()
+    # attention of two layers on sampled sequences
+    seqs = [0, int(np.argmax(s.prompt_lens))]
+    for l in (0, 1):
+        li = AttnInputs(s, "dual", inp.q, inp.k_new, inp.v_new, inp.k_cache * (2.0 ** -(l % 3)), inp.v_cache)
+        ref = oracle_attn_subset(li, seqs)
+        out = outs[l].float().cpu().numpy().astype(np.float64)
+        check_attn(out, ref, li, seqs=seqs, label=f"c5 step layer {l}")
+    # unmask decisions
+    ref = unmask_ref(logits, tokens, mask, s.prompt_lens, s.gen_len, s.block_size, s.block_idxs, 0.7,
+                     advance=True)
+    # the conf output was not requested in this step: compare decisions only
+    g = dict(tokens=tk.cpu().numpy(), mask=mk.cpu().numpy(), n_decoded=nd.cpu().numpy(),
+             decoded_pos=dp.cpu().numpy(), conf=ref.conf.copy())
+    compare_unmask(g, ref, s, label="c5 step")
+    done = sorted(int(x) for x in ds.cpu().numpy()[:int(nn.item())])
+    if not ref.tie_step.any() and not ref.tie_tau.any():
+        assert done == list(ref.done_seqs)
+    # refreshed sequences' caches equal the source on every layer; others untouched
+    ks_t = k_src.transpose(1, 2)
+    for l in (0, 13, 27):
+        for i in range(s.batch):
+            L = int(s.prompt_lens[i]) + s.gen_len
+            if i in done:
+                assert torch.equal(kcs[l][i, :, :L], ks_t[i, :, :L])
+            else:
+                assert torch.equal(kcs[l][i], kc0[i] * (2.0 ** -(l % 3)))
+    say(f"  c5 step: {len(done)} sequences finished their block and were refreshed")

@@ -28,6 +28,7 @@ Conventions (all arrays are numpy):
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
@@ -49,33 +50,67 @@ def rng_for(*ids: int) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([BASE_SEED, *[int(i) for i in ids]]))
 
 
-def bf16_round(x: np.ndarray) -> np.ndarray:
+def bf16_round(x: np.ndarray, inplace: bool = False) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even).
 
     Returns float32 values that are exactly representable in bfloat16.
-    Inputs must be finite.
+    Inputs must be finite.  ``inplace`` rounds a C-contiguous float32 array
+    in place.
     """
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    u = ((u + 0x7FFF + lsb) >> 16) << 16
-    return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+    if not (inplace and x.dtype == np.float32 and x.flags.c_contiguous):
+        x = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = x.reshape(-1).view(np.uint32)
+    step = 1 << 24
+    for s in range(0, u.size, step):   # chunked: bounded temporaries
+        c = u[s:s + step]
+        lsb = (c >> 16) & np.uint32(1)
+        c += np.uint32(0x7FFF)          # finite values cannot overflow 32 bits
+        c += lsb
+        c &= np.uint32(0xFFFF0000)
+    return x
 
 
-def quantise(x: np.ndarray, dtype: str) -> np.ndarray:
+def quantise(x: np.ndarray, dtype: str, inplace: bool = False) -> np.ndarray:
     if dtype == "bf16":
-        return bf16_round(x)
+        return bf16_round(x, inplace)
     if dtype == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def normal(shape, sigma: float, dtype: str, *ids: int) -> np.ndarray:
-    g = rng_for(*ids)
-    x = g.standard_normal(size=shape, dtype=np.float32)
+_CHUNK = 1 << 22
+
+
+def _fill_chunk(flat: np.ndarray, sigma: float, dtype: str, ids, c: int):
+    part = flat[c * _CHUNK:(c + 1) * _CHUNK]
+    rng_for(*ids, c).standard_normal(out=part, dtype=np.float32)
     if sigma != 1.0:
-        x *= np.float32(sigma)
-    return quantise(x, dtype)
+        part *= np.float32(sigma)
+    if dtype == "bf16":
+        bf16_round(part, inplace=True)
+
+
+def normal(shape, sigma: float, dtype: str, *ids: int) -> np.ndarray:
+    """N(0, sigma) float32 array quantised to ``dtype``.
+
+    The flattened array is drawn in chunks of 2^22 values; chunk c uses the
+    generator keyed by (*ids, c), so the result does not depend on how many
+    threads fill it.
+    """
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    x = np.empty(shape, np.float32)
+    flat = x.reshape(-1)
+    n_chunks = (flat.size + _CHUNK - 1) // _CHUNK
+    if n_chunks <= 1:
+        for c in range(n_chunks):
+            _fill_chunk(flat, sigma, dtype, ids, c)
+    else:
+        import concurrent.futures
+        workers = min(16, len(os.sched_getaffinity(0)), n_chunks)
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda c: _fill_chunk(flat, sigma, dtype, ids, c), range(n_chunks)))
+    return x
 
 
 # --------------------------------------------------------------------------
@@ -235,33 +270,54 @@ def make_logits(shape: Shape, recipe: str = "auto", step: int = 0, variant: int 
       quantisation.  This makes threshold sweeps decode meaningful numbers
       of tokens; ``calibrated_targets`` returns the u values.
     * ``"auto"``: ``spike`` for config 1, ``peak`` otherwise.
+
+    Row r = i * B + t draws its background from the generator keyed by
+    (config, variant, step, r).
     """
     s = shape
     dt = dtype or s.dtype
     if recipe == "auto":
         recipe = "spike" if s.cfg_id == 1 else "peak"
+    if recipe not in ("spike", "peak", "calibrated"):
+        raise ValueError(recipe)
     ids = (s.cfg_id, variant, step)
     b, B, V = s.batch, s.block_size, s.vocab
-    g = rng_for(*ids, _T_LOG)
-    sigma = 2.0 if recipe == "spike" else 3.0
-    x = g.standard_normal(size=(b, B, V), dtype=np.float32)
-    x *= np.float32(sigma)
-    tok = rng_for(*ids, _T_PEAKTOK).integers(0, V, size=(b, B))
-    bi, ti = np.meshgrid(np.arange(b), np.arange(B), indexing="ij")
+    sigma = np.float32(2.0 if recipe == "spike" else 3.0)
+    x = np.empty((b, B, V), np.float32)
+    rows = x.reshape(b * B, V)
+    tok = rng_for(*ids, _T_PEAKTOK).integers(0, V, size=(b, B)).reshape(-1)
     if recipe == "spike":
-        on = rng_for(*ids, _T_SPIKE).random(size=(b, B)) < 0.4
-        x[bi, ti, tok] += np.where(on, np.float32(8.0), np.float32(0.0)).astype(np.float32)
+        on = rng_for(*ids, _T_SPIKE).random(size=(b, B)).reshape(-1) < 0.4
+        add = np.where(on, np.float32(8.0), np.float32(0.0)).astype(np.float32)
     elif recipe == "peak":
-        h = rng_for(*ids, _T_PEAKH).uniform(0.0, 12.0, size=(b, B)).astype(np.float32)
-        x[bi, ti, tok] += h
-    elif recipe == "calibrated":
-        u = calibrated_targets(s, step, variant)
-        x[bi, ti, tok] = -np.inf
-        rest = np.logaddexp.reduce(x.astype(np.float64), axis=-1)
-        x[bi, ti, tok] = (rest + np.log(u / (1.0 - u))).astype(np.float32)
+        add = rng_for(*ids, _T_PEAKH).uniform(0.0, 12.0, size=(b, B)).astype(np.float32).reshape(-1)
     else:
-        raise ValueError(recipe)
-    return quantise(x, dt)
+        u = calibrated_targets(s, step, variant).reshape(-1)
+
+    def fill(r):
+        row = rows[r]
+        rng_for(*ids, _T_LOG, r).standard_normal(out=row, dtype=np.float32)
+        row *= sigma
+        if recipe == "calibrated":
+            row[tok[r]] = -np.inf
+            m = float(row.max())
+            rest = m + np.log(np.exp(row.astype(np.float64) - m).sum())
+            row[tok[r]] = np.float32(rest + np.log(u[r] / (1.0 - u[r])))
+        else:
+            row[tok[r]] += add[r]
+        if dt == "bf16":
+            bf16_round(row, inplace=True)
+
+    n = b * B
+    if n * V <= (1 << 22):
+        for r in range(n):
+            fill(r)
+    else:
+        import concurrent.futures
+        workers = min(16, len(os.sched_getaffinity(0)))
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(n)))
+    return x
 
 
 def calibrated_targets(shape: Shape, step: int = 0, variant: int = 0) -> np.ndarray:
