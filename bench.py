@@ -17,8 +17,10 @@ pair, so every step sees the first step after a refresh (all 32 block
 positions masked).
 
 The K timed steps are captured once in a HIP graph and replayed between two
-device synchronisations.  Per-kernel durations come from HIP events recorded
-between the kernels of the same graph on the launch stream.
+device synchronisations.  Per-kernel durations come from a second pass over
+the same K steps in which every kernel is launched with its own start/stop
+HIP events (libfdllm's timing hook, hipExtLaunchKernel), on the stream it
+runs on.
 
 Prints one JSON line.  --gpus N > 1 is refused: this path runs on one GPU.
 """
@@ -139,17 +141,46 @@ class Bench:
         ]
 
     def run_steps(self, first_step, n_steps, events=None):
+        """Launch the block-steps; with `events`, every kernel records its own
+        start/stop HIP events (kernel n uses events 2n and 2n+1)."""
         names = []
         for st in range(first_step, first_step + n_steps):
             for k in range(N_BLOCKS):
                 for name, fn in self.launches(st * N_BLOCKS + k):
                     if events is not None:
-                        events[len(names)].record()
+                        n = len(names)
+                        self.fd.set_timing_events(events.ev[2 * n], events.ev[2 * n + 1])
                     fn()
                     names.append(name)
-        if events is not None:
-            events[len(names)].record()
         return names
+
+
+class HipEvents:
+    """Timing events from the HIP runtime torch loaded (shared soname)."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e.value)
+
+    def elapsed_s(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[a], self.ev[b])
+        assert rc == 0, f"hipEventElapsedTime failed ({rc})"
+        return ms.value * 1e-3
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
 
 
 def cpu_baseline(seconds: float):
@@ -199,8 +230,9 @@ def main():
     K, W = args.steps, args.warmup
     use_graph = not args.no_graph
     n_k = K * N_BLOCKS * 3
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(n_k + 1)]
+    events = HipEvents(2 * n_k)
 
+    # timed region: K steps replayed from one HIP graph (or launched eagerly)
     if use_graph:
         stream = torch.cuda.Stream()
         with torch.cuda.stream(stream):
@@ -210,9 +242,6 @@ def main():
             g_timed = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g_timed, stream=stream):
                 b.run_steps(W, K)
-            g_ev = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_ev, stream=stream):
-                names = b.run_steps(W, K, events)
         torch.cuda.synchronize()
         b.reset_state()
         torch.cuda.synchronize()
@@ -222,10 +251,6 @@ def main():
         g_timed.replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        b.reset_state()
-        torch.cuda.synchronize()
-        g_ev.replay()
-        torch.cuda.synchronize()
     else:
         b.run_steps(0, W)
         torch.cuda.synchronize()
@@ -233,15 +258,18 @@ def main():
         b.run_steps(W, K)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        b.reset_state()
-        torch.cuda.synchronize()
-        names = b.run_steps(W, K, events)
-        torch.cuda.synchronize()
+    # the same K steps again, launched on the default stream with every
+    # kernel bracketed by its own start/stop events
+    b.reset_state()
+    torch.cuda.synchronize()
+    names = b.run_steps(W, K, events)
+    torch.cuda.synchronize()
 
     elapsed = t1 - t0
     per = {}
     for n, name in enumerate(names):
-        per.setdefault(name, []).append(events[n].elapsed_time(events[n + 1]) * 1e-3)
+        per.setdefault(name, []).append(events.elapsed_s(2 * n, 2 * n + 1))
+    events.close()
     kernels = {}
     for name, ts in per.items():
         avg = sum(ts) / len(ts)

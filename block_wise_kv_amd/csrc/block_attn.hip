@@ -33,6 +33,7 @@
 // f32 (any mode, d = 64 or 128): a plain VALU kernel, one wave per query
 // row, fp32 throughout.
 #include <float.h>
+#include <stdlib.h>
 
 #include "fdllm_device.h"
 #include "fdllm_internal.h"
@@ -47,6 +48,7 @@ constexpr int kD = 128;                // head dim (bf16 path)
 constexpr int kVtStride = 36;          // bf16 per d-row of the transposed V tile
 constexpr int kRedStride = 65;         // floats per query row of the merge buffer
 constexpr int kPartFloats = kQT * kD + 2 * kQT;  // one split partial: O, m, l
+constexpr int kMaxSplit = 8;           // key chunks per (sequence, head, query tile)
 
 struct Geo {
   int i, h, hk, qt, s;
@@ -92,11 +94,16 @@ __device__ __forceinline__ bool decode_item(const AttnArgs& a, int item, Geo& g)
   return true;
 }
 
+// Address of K/V row j: the fresh tensor inside [a0, a1), the cache
+// elsewhere.  Branch-free (an integer select), so that loads issued for
+// different rows stay in one basic block and in flight together.
 template <typename T>
 __device__ __forceinline__ const T* kv_row(const AttnArgs& a, const T* fresh, const T* cache, const Geo& g,
                                            int j, int d) {
-  if (j >= g.a0 && j < g.a1) return fresh + (((size_t)g.i * a.fresh_rows + (j - g.a0)) * a.Hkv + g.hk) * d;
-  return cache + (((size_t)g.i * a.Hkv + g.hk) * a.sq.Lcap + j) * d;
+  const bool fr = (unsigned)(j - g.a0) < (unsigned)(g.a1 - g.a0);
+  const uintptr_t pf = (uintptr_t)(fresh + (((size_t)g.i * a.fresh_rows + (j - g.a0)) * a.Hkv + g.hk) * d);
+  const uintptr_t pc = (uintptr_t)(cache + (((size_t)g.i * a.Hkv + g.hk) * a.sq.Lcap + j) * d);
+  return (const T*)(fr ? pf : pc);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
@@ -118,7 +125,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_vt_raw[kNW * kD * kVtStride];
   __shared__ float s_m[kNW][kQT], s_l[kNW][kQT];
   __shared__ float s_L[kQT];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lq = lane & 31, hh = lane >> 5;
@@ -132,19 +138,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* vcp = (const uint16_t*)a.vc;
 
   // Q as the B operand of S^T = K Q^T: lane (lq, hh) holds query row lq,
-  // columns [16 ks + 8 hh, +8) for ks = 0..7.
+  // columns [16 ks + 8 hh, +8) for ks = 0..7.  Rows past nq are zero.
   bf16x8 qop[8];
   {
     const int r = q0 + lq;
-    if (r < g.nq) {
-      const uint16_t* qrow = qp + (((size_t)g.i * a.fresh_rows + r) * a.Hq + g.h) * kD;
+    const uint16_t* qrow = qp + (((size_t)g.i * a.fresh_rows + min(r, g.nq - 1)) * a.Hq + g.h) * kD;
+    const bool live = r < g.nq;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qop[ks] = as_bf16x8(*(const uint4*)(qrow + 16 * ks + 8 * hh));
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qop[ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 w = *(const uint4*)(qrow + 16 * ks + 8 * hh);
+      qop[ks] = as_bf16x8(live ? w : make_uint4(0, 0, 0, 0));
     }
   }
+
+  // K rows of a sub-tile go to A-operand registers; V rows (keys 16 n +
+  // 4 (lane / 16) + kk, columns 8 (lane % 16) + [0, 8)) to registers for the
+  // LDS transpose.  Rows past the chunk end re-read its last row (masked
+  // later), so every load is unconditional.
+  bf16x8 kop[8];
+  uint4 vr[2][4];
+  auto load_tile = [&](int t0) {
+    const uint16_t* krow = kv_row(a, knp, kcp, g, min(t0 + lq, g.ke - 1), kD);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kop[ks] = as_bf16x8(*(const uint4*)(krow + 16 * ks + 8 * hh));
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int j = min(t0 + 16 * n + 4 * (lane >> 4) + kk, g.ke - 1);
+        vr[n][kk] = *(const uint4*)(kv_row(a, vnp, vcp, g, j, kD) + 8 * (lane & 15));
+      }
+  };
 
   f32x16 O[4];
 #pragma unroll
@@ -154,30 +178,38 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   uint16_t* vt = s_vt_raw + wid * (kD * kVtStride);
 
-  for (int kt = g.kb + kKT * wid; kt < g.ke; kt += kKT * kNW) {
-    // K rows -> A operand registers
-    bf16x8 kop[8];
-    {
-      const int j = min(kt + lq, g.ke - 1);
-      const uint16_t* krow = kv_row(a, knp, kcp, g, j, kD);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) kop[ks] = as_bf16x8(*(const uint4*)(krow + 16 * ks + 8 * hh));
-    }
-    // V rows: lane loads keys 16 n + 4 (lane / 16) + kk, columns 8 (lane % 16) + [0, 8)
-    uint4 vr[2][4];
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int j = min(kt + 16 * n + 4 * (lane >> 4) + kk, g.ke - 1);
-        vr[n][kk] = *(const uint4*)(kv_row(a, vnp, vcp, g, j, kD) + 8 * (lane & 15));
-      }
-
+  int kt = g.kb + kKT * wid;
+  load_tile(kt);
+  for (; kt < g.ke; kt += kKT * kNW) {
     f32x16 S;
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S, 0, 0, 0);
+
+    // V transposed into LDS: vt[d][key], 4 keys per 8-byte write
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const uint32_t* w0 = (const uint32_t*)&vr[n][0];
+      const uint32_t* w1 = (const uint32_t*)&vr[n][1];
+      const uint32_t* w2 = (const uint32_t*)&vr[n][2];
+      const uint32_t* w3 = (const uint32_t*)&vr[n][3];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) ? 16 : 0;
+        const uint32_t b0 = (w0[e >> 1] >> sh) & 0xffffu;
+        const uint32_t b1 = (w1[e >> 1] >> sh) & 0xffffu;
+        const uint32_t b2 = (w2[e >> 1] >> sh) & 0xffffu;
+        const uint32_t b3 = (w3[e >> 1] >> sh) & 0xffffu;
+        uint2 v2;
+        v2.x = b0 | (b1 << 16);
+        v2.y = b2 | (b3 << 16);
+        *(uint2*)(vt + (8 * (lane & 15) + e) * kVtStride + 16 * n + 4 * (lane >> 4)) = v2;
+      }
+    }
+    // K and V of this sub-tile are consumed: fetch the next one while the
+    // softmax and the PV product run
+    load_tile(kt + kKT * kNW);
 
     // lane holds query column lq, keys kt + 8 (r / 4) + 4 hh + (r % 4)
     float mx = -INFINITY;
@@ -214,27 +246,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       w.z = pack_bf16x2(p[8 * h2 + 4], p[8 * h2 + 5]);
       w.w = pack_bf16x2(p[8 * h2 + 6], p[8 * h2 + 7]);
       pop[h2] = as_bf16x8(w);
-    }
-
-    // V transposed into LDS: vt[d][key], 4 keys per 8-byte write
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const uint32_t* w0 = (const uint32_t*)&vr[n][0];
-      const uint32_t* w1 = (const uint32_t*)&vr[n][1];
-      const uint32_t* w2 = (const uint32_t*)&vr[n][2];
-      const uint32_t* w3 = (const uint32_t*)&vr[n][3];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) ? 16 : 0;
-        const uint32_t b0 = (w0[e >> 1] >> sh) & 0xffffu;
-        const uint32_t b1 = (w1[e >> 1] >> sh) & 0xffffu;
-        const uint32_t b2 = (w2[e >> 1] >> sh) & 0xffffu;
-        const uint32_t b3 = (w3[e >> 1] >> sh) & 0xffffu;
-        uint2 v2;
-        v2.x = b0 | (b1 << 16);
-        v2.y = b2 | (b3 << 16);
-        *(uint2*)(vt + (8 * (lane & 15) + e) * kVtStride + 16 * n + 4 * (lane >> 4)) = v2;
-      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -274,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 
   float* red = (float*)s_vt_raw;  // [kNW][kQT][kRedStride], reuses the V tiles
   const bool split = a.n_split > 1;
-  const size_t slot = (((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt) * a.n_split + g.s;
+  const size_t slot = (((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt) * a.n_split + g.s;  // (i, h, qt, s)
   float* part = split ? a.part + slot * kPartFloats : nullptr;
   const int oq = tid >> 3;          // query row handled in the output phase
   const int od = 8 * (tid & 7);     // 8 columns within the 64-column half
@@ -317,63 +328,74 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     }
     __syncthreads();
   }
-  if (!split) return;
-
-  if (wid == 0 && hh == 0) {
+  if (split && wid == 0 && hh == 0) {
     part[kQT * kD + lq] = M;
     part[kQT * kD + kQT + lq] = Lsum;
   }
-  __syncthreads();
-  uint32_t* cnt = a.cnt + ((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt;
-  if (tid == 0) {
-    __threadfence();
-    const unsigned old = atomicAdd(cnt, 1u);
-    s_last = (old == (unsigned)g.n_act - 1u);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
-  // ---- last workgroup: merge the n_act split partials of this tile
-  const float* part0 = a.part + (slot - g.s) * kPartFloats;
+// Merge the split-key partials of one (sequence, head, query tile): the
+// second kernel of a split launch, so the partials written with ordinary
+// stores by the first are visible here.  Every partial load is issued
+// before any is used (clamped index, weight 0 past the active splits).
+__global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
+  const int item = blockIdx.x;  // (i, h, qt)
+  const int qt = item % a.n_qt;
+  const int h = (item / a.n_qt) % a.Hq;
+  const int i = item / (a.n_qt * a.Hq);
+  const int P = seq_prompt(a.sq, i);
+  int a0, a1;
+  fresh_range(a.mode, P, a.sq.G, a.sq.B, seq_block(a.sq, i), a0, a1);
+  const int nq = a1 - a0, q0 = qt * kQT;
+  const int tid = threadIdx.x;
   const int cq = tid >> 3;            // query row
   const int cd = 16 * (tid & 7);      // 16 columns
-  if (q0 + cq < g.nq) {
-    float Mg = -INFINITY;
-    for (int s = 0; s < g.n_act; ++s) Mg = fmaxf(Mg, part0[s * kPartFloats + kQT * kD + cq]);
-    float wsum = 0.f;
-    float o[16];
+  if (q0 + cq >= nq) return;
+  const int n_act = (P + a.sq.G + a.kchunk - 1) / a.kchunk;
+  const float c = a.scale_log2;
+  const float* part0 = a.part + (size_t)item * a.n_split * kPartFloats;
+  float ms[kMaxSplit], ls[kMaxSplit];
+  float4 xs[kMaxSplit][4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[e] = 0.f;
-    for (int s = 0; s < g.n_act; ++s) {
-      const float* ps = part0 + s * kPartFloats;
-      const float w = exp2_fast((ps[kQT * kD + cq] - Mg) * c);
-      wsum += ps[kQT * kD + kQT + cq] * w;
-      const float4* src = (const float4*)(ps + cq * kD + cd);
+  for (int s = 0; s < kMaxSplit; ++s) {
+    const float* ps = part0 + min(s, n_act - 1) * kPartFloats;
+    ms[s] = ps[kQT * kD + cq];
+    ls[s] = ps[kQT * kD + kQT + cq];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float4 x = src[v];
-        o[4 * v + 0] += x.x * w;
-        o[4 * v + 1] += x.y * w;
-        o[4 * v + 2] += x.z * w;
-        o[4 * v + 3] += x.w * w;
-      }
-    }
-    const float inv = 1.f / wsum;
-    uint16_t* orow = (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + cq) * a.Hq + g.h) * kD;
-    uint4 w0, w1;
-    w0.x = pack_bf16x2(o[0] * inv, o[1] * inv);
-    w0.y = pack_bf16x2(o[2] * inv, o[3] * inv);
-    w0.z = pack_bf16x2(o[4] * inv, o[5] * inv);
-    w0.w = pack_bf16x2(o[6] * inv, o[7] * inv);
-    w1.x = pack_bf16x2(o[8] * inv, o[9] * inv);
-    w1.y = pack_bf16x2(o[10] * inv, o[11] * inv);
-    w1.z = pack_bf16x2(o[12] * inv, o[13] * inv);
-    w1.w = pack_bf16x2(o[14] * inv, o[15] * inv);
-    *(uint4*)(orow + cd) = w0;
-    *(uint4*)(orow + cd + 8) = w1;
+    for (int v = 0; v < 4; ++v) xs[s][v] = *(const float4*)(ps + cq * kD + cd + 4 * v);
   }
-  if (tid == 0) *cnt = 0u;
+  float Mg = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) Mg = fmaxf(Mg, ms[s]);
+  float wsum = 0.f;
+  float o[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    const float w = (s < n_act) ? exp2_fast((ms[s] - Mg) * c) : 0.f;
+    wsum += ls[s] * w;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      o[4 * v + 0] += xs[s][v].x * w;
+      o[4 * v + 1] += xs[s][v].y * w;
+      o[4 * v + 2] += xs[s][v].z * w;
+      o[4 * v + 3] += xs[s][v].w * w;
+    }
+  }
+  const float inv = 1.f / wsum;
+  uint16_t* orow = (uint16_t*)a.out + (((size_t)i * a.fresh_rows + q0 + cq) * a.Hq + h) * kD;
+  uint4 w0, w1;
+  w0.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+  w0.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+  w0.z = pack_bf16x2(o[4] * inv, o[5] * inv);
+  w0.w = pack_bf16x2(o[6] * inv, o[7] * inv);
+  w1.x = pack_bf16x2(o[8] * inv, o[9] * inv);
+  w1.y = pack_bf16x2(o[10] * inv, o[11] * inv);
+  w1.z = pack_bf16x2(o[12] * inv, o[13] * inv);
+  w1.w = pack_bf16x2(o[14] * inv, o[15] * inv);
+  *(uint4*)(orow + cd) = w0;
+  *(uint4*)(orow + cd + 8) = w1;
 }
 
 // ------------------------------------------------------------------ f32 VALU
@@ -447,6 +469,17 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ planning
+// Workgroups the key-split aims for (about two per CU by default; the
+// environment variable FDLLM_ATTN_TARGET_WGS overrides it for tuning).
+static long attn_target_workgroups() {
+  static long v = [] {
+    const char* e = getenv("FDLLM_ATTN_TARGET_WGS");
+    long t = e ? atol(e) : 512;
+    return t > 0 ? t : 512;
+  }();
+  return v;
+}
+
 AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max) {
   (void)Hkv;
   (void)d;
@@ -464,10 +497,11 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   const long base = (long)b * Hq * p.n_qt;
   const int unit = kKT * kNW;  // 128 keys: one sub-tile per wave
   const int max_split = (L_max + unit - 1) / unit;
-  const long target = 512;     // about two workgroups per CU
+  const long target = attn_target_workgroups();
   int ns = (int)((target + base - 1) / base);
   if (ns < 1) ns = 1;
   if (ns > max_split) ns = max_split;
+  if (ns > kMaxSplit) ns = kMaxSplit;
   int kchunk = (L_max + ns - 1) / ns;
   kchunk = ((kchunk + unit - 1) / unit) * unit;
   ns = (L_max + kchunk - 1) / kchunk;
@@ -478,22 +512,26 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   p.grid = p.per_xcd * 8;
   if (ns > 1) {
     const size_t slots = (size_t)base * ns;
-    size_t bytes = slots * kPartFloats * sizeof(float);
-    bytes += (size_t)base * sizeof(uint32_t);
+    const size_t bytes = slots * kPartFloats * sizeof(float);
     p.ws_bytes = (bytes + 255) & ~(size_t)255;
   }
   return p;
 }
 
 hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, int d, hipStream_t st) {
+  const LaunchEvents ev = take_launch_events();
   if (dtype == 0) {
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)p.grid), dim3(kThreads), 0, st, a);
-  } else {
-    dim3 grid((unsigned)p.n_qt, (unsigned)a.Hq, (unsigned)a.sq.b);
-    if (d == 64) hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(256), 0, st, a);
+    if (p.n_split == 1)
+      return launch_kernel(attn_bf16_kernel, dim3((unsigned)p.grid), dim3(kThreads), 0, st, ev.start, ev.stop, a);
+    hipError_t e = launch_kernel(attn_bf16_kernel, dim3((unsigned)p.grid), dim3(kThreads), 0, st, ev.start,
+                                 (hipEvent_t) nullptr, a);
+    if (e != hipSuccess) return e;
+    const unsigned tiles = (unsigned)(a.sq.b * a.Hq * p.n_qt);
+    return launch_kernel(attn_combine_kernel, dim3(tiles), dim3(kThreads), 0, st, (hipEvent_t) nullptr, ev.stop, a);
   }
-  return hipGetLastError();
+  dim3 grid((unsigned)p.n_qt, (unsigned)a.Hq, (unsigned)a.sq.b);
+  return d == 64 ? launch_kernel(attn_f32_kernel<64>, grid, dim3(256), 0, st, ev.start, ev.stop, a)
+                 : launch_kernel(attn_f32_kernel<128>, grid, dim3(256), 0, st, ev.start, ev.stop, a);
 }
 
 }  // namespace fdllm

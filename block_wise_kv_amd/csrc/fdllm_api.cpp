@@ -16,6 +16,8 @@ using namespace fdllm;
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t g_timing_start = nullptr;
+thread_local hipEvent_t g_timing_stop = nullptr;
 
 fdllm_status fail(fdllm_status st, const char* fmt, ...) {
   char buf[512];
@@ -151,8 +153,10 @@ fdllm_status setup_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t dtyp
   if (dtype != FDLLM_BF16 && dtype != FDLLM_F32) return fail(FDLLM_ERR_INVALID_ARG, "logits dtype %d invalid", dtype);
   if (seq->block_size > 1024) return fail(FDLLM_ERR_UNSUPPORTED, "block_size > 1024");
   if (seq->batch > 65535) return fail(FDLLM_ERR_UNSUPPORTED, "batch > 65535");
-  su.chunk = unmask_chunk_elems(dtype, vocab, seq->batch * seq->block_size);
-  su.nchunk = (vocab + su.chunk - 1) / su.chunk;
+  if (vocab > 256 * 8192) return fail(FDLLM_ERR_UNSUPPORTED, "vocab > 2097152");
+  const UnmaskPlan up = plan_unmask(dtype, vocab, seq->batch * seq->block_size);
+  su.chunk = up.chunk;
+  su.nchunk = up.nchunk;
   if ((int64_t)su.nchunk * seq->block_size >= ((int64_t)1 << 31) - 1)
     return fail(FDLLM_ERR_INVALID_ARG, "vocab too large");
   su.ws = unmask_workspace_bytes(seq->batch, seq->block_size, su.nchunk);
@@ -161,7 +165,21 @@ fdllm_status setup_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t dtyp
 
 }  // namespace
 
+namespace fdllm {
+LaunchEvents take_launch_events() {
+  LaunchEvents e{g_timing_start, g_timing_stop};
+  g_timing_start = g_timing_stop = nullptr;
+  return e;
+}
+}  // namespace fdllm
+
 extern "C" {
+
+fdllm_status fdllm_set_timing_events(void* start_event, void* stop_event) {
+  g_timing_start = (hipEvent_t)start_event;
+  g_timing_stop = (hipEvent_t)stop_event;
+  return ok();
+}
 
 size_t fdllm_block_attn_workspace(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode,
                                   int32_t fresh_rows) {
@@ -217,9 +235,7 @@ fdllm_status fdllm_block_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
   a.n_items = su.plan.n_items;
   a.per_xcd = su.plan.per_xcd;
   if (su.plan.ws_bytes > 0) {
-    const size_t slots = (size_t)su.plan.n_items;
     a.part = (float*)workspace;
-    a.cnt = (uint32_t*)((char*)workspace + slots * (size_t)(32 * 128 + 64) * sizeof(float));
   }
   hipError_t e = launch_block_attn(a, su.plan, attn->dtype, attn->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "block_attn launch failed: %s", hipGetErrorString(e));
@@ -262,6 +278,7 @@ fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, in
   a.seq_stride = seq_stride;
   a.row_stride = row_stride;
   a.logits = logits;
+  a.vec = vec ? 1 : 0;
   a.tau = threshold;
   a.flags = flags;
   a.tokens = tokens;
@@ -273,15 +290,18 @@ fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, in
   a.n_done = n_done;
   a.nchunk = su.nchunk;
   a.chunk = su.chunk;
+  const size_t rows = (size_t)seq->batch * seq->block_size;
   char* w = (char*)workspace;
   a.part = (UnmaskPartial*)w;
-  w += (size_t)seq->batch * seq->block_size * su.nchunk * sizeof(UnmaskPartial);
+  w += (rows * su.nchunk + rows) * sizeof(UnmaskPartial);
+  a.done_flag = (int32_t*)w;
+  w += (size_t)seq->batch * 8;
+  a.row_cnt = (uint32_t*)w;
+  w += rows * 4;
   a.seq_cnt = (uint32_t*)w;
   w += (size_t)seq->batch * 4;
   a.glob_cnt = (uint32_t*)w;
-  w += 16;
-  a.done_flag = (int32_t*)w;
-  hipError_t e = launch_unmask(a, logits_dtype, vec, (hipStream_t)stream);
+  hipError_t e = launch_unmask(a, logits_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "unmask launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -53,4 +53,44 @@ __device__ __forceinline__ int wave_min_i(int v) {
   return v;
 }
 
+// ---- cross-workgroup publication without cache write-back / invalidate.
+// Data published to other workgroups is written with agent-scope atomic
+// stores (write-through to the device coherence point), the writer waits for
+// their completion, then bumps a relaxed agent-scope counter; the last
+// arriver reads the data back with agent-scope atomic loads.
+__device__ __forceinline__ void st_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coherent(const uint64_t* p) {
+  return __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent_f2(float* p, float a, float b) {
+  st_coherent((uint64_t*)p, (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32));
+}
+__device__ __forceinline__ void ld_coherent_f2(const float* p, float& a, float& b) {
+  const uint64_t w = ld_coherent((const uint64_t*)p);
+  a = __uint_as_float((uint32_t)w);
+  b = __uint_as_float((uint32_t)(w >> 32));
+}
+// Wait until this thread's memory operations have completed, then add 1 to
+// the counter; returns the previous count.
+__device__ __forceinline__ unsigned arrive(uint32_t* cnt) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every thread of the workgroup waits for its own stores, then thread 0
+// arrives; returns (to all threads) whether this workgroup was the last of
+// `expected` arrivals.
+__device__ __forceinline__ bool block_arrive(uint32_t* cnt, unsigned expected, int* s_flag) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) *s_flag = (arrive(cnt) == expected - 1u);
+  __syncthreads();
+  return *s_flag != 0;
+}
+
 }  // namespace fdllm

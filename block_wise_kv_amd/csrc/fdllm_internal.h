@@ -2,6 +2,7 @@
 // units of libfdllm.  Not installed; the public ABI is include/fdllm.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -71,6 +72,7 @@ struct UnmaskArgs {
   int V;
   int64_t seq_stride, row_stride;  // elements
   const void* logits;
+  int vec;                  // 1: 16-byte vector loads (aligned rows)
   float tau;
   uint32_t flags;
   int32_t* tokens;
@@ -80,16 +82,20 @@ struct UnmaskArgs {
   double* conf;
   int32_t* done_seqs;
   int32_t* n_done;
-  UnmaskPartial* part;      // [b][B][nchunk]
+  UnmaskPartial* part;      // [b][B][nchunk] chunk partials, then [b][B] row results
+  int32_t* done_flag;       // [b] x 8 bytes
+  uint32_t* row_cnt;        // [b][B]
   uint32_t* seq_cnt;        // [b]
   uint32_t* glob_cnt;       // [1]
-  int32_t* done_flag;       // [b]
-  int nchunk;
-  int chunk;                // vocab entries per chunk
+  int nchunk;               // vocab chunks per row (one workgroup each)
+  int chunk;                // vocab entries per chunk (multiple of the vector width)
 };
+struct UnmaskPlan {
+  int nchunk, chunk;
+};
+UnmaskPlan plan_unmask(int dtype, int V, int rows);
 size_t unmask_workspace_bytes(int b, int B, int nchunk);
-int unmask_chunk_elems(int dtype, int V, int rows);
-hipError_t launch_unmask(const UnmaskArgs& a, int dtype, bool vec, hipStream_t st);
+hipError_t launch_unmask(const UnmaskArgs& a, int dtype, hipStream_t st);
 
 // ------------------------------------------------------------------ attention
 struct AttnArgs {
@@ -105,8 +111,7 @@ struct AttnArgs {
   const void* kc;
   const void* vc;
   void* out;
-  float* part;              // split-key partials (null when n_split == 1)
-  uint32_t* cnt;            // split-key counters [b][Hq][n_qt]
+  float* part;              // split-key partials [b][Hq][n_qt][n_split] (null when n_split == 1)
   int n_qt;                 // query tiles per (sequence, head)
   int n_split;              // key chunks per (sequence, head, query tile)
   int kchunk;               // keys per chunk
@@ -123,5 +128,27 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, in
 
 // ------------------------------------------------------------------ misc
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// Measurement hook (fdllm_set_timing_events): returns the armed start/stop
+// events of the calling host thread (null when not armed) and disarms it.
+struct LaunchEvents {
+  hipEvent_t start, stop;
+};
+LaunchEvents take_launch_events();
+
+// Launch `kernel` on `st`.  With a start and/or stop event, the launch
+// records them at the kernel's start / end (hipExtLaunchKernel).  A call that
+// runs several kernels passes the start event to the first and the stop
+// event to the last.
+template <typename... Args>
+hipError_t launch_kernel(void (*kernel)(Args...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t st,
+                         hipEvent_t ev_start, hipEvent_t ev_stop, Args... args) {
+  if (ev_start || ev_stop) {
+    void* argv[] = {(void*)&args...};
+    return hipExtLaunchKernel((const void*)kernel, grid, block, argv, shmem, st, ev_start, ev_stop, 0);
+  }
+  hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+  return hipGetLastError();
+}
 
 }  // namespace fdllm

@@ -68,8 +68,8 @@ hipError_t launch_kv_refresh(const RefreshArgs& a, int max_rows, hipStream_t st)
   const unsigned gx = (unsigned)((nvec + per_block - 1) / per_block);
   if (gx == 0) return hipSuccess;
   dim3 grid(gx, (unsigned)a.sq.b, 1);
-  hipLaunchKernelGGL(kv_refresh_kernel, grid, dim3(kRefreshThreads), 0, st, a);
-  return hipGetLastError();
+  const LaunchEvents ev = take_launch_events();
+  return launch_kernel(kv_refresh_kernel, grid, dim3(kRefreshThreads), 0, st, ev.start, ev.stop, a);
 }
 
 // ------------------------------------------------------------------ zero fill
@@ -84,8 +84,8 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   if (n == 0) return hipSuccess;
   size_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (uint32_t*)p, n);
-  return hipGetLastError();
+  const LaunchEvents ev = take_launch_events();
+  return launch_kernel(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, ev.start, ev.stop, (uint32_t*)p, n);
 }
 
 }  // namespace fdllm

@@ -68,6 +68,7 @@ _SIGS = [
     ("fdllm_kv_refresh", ctypes.c_int32,
      [ctypes.POINTER(SeqDesc), ctypes.POINTER(AttnDesc), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
     ("fdllm_workspace_init", ctypes.c_int32, [_P, ctypes.c_size_t, _P]),
+    ("fdllm_set_timing_events", ctypes.c_int32, [_P, _P]),
     ("fdllm_status_string", ctypes.c_char_p, [ctypes.c_int32]),
     ("fdllm_last_error", ctypes.c_char_p, []),
     ("fdllm_version", ctypes.c_int32, []),
@@ -78,6 +79,10 @@ def lib():
     """Load libfdllm.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        try:  # share torch's HIP runtime (same soname) when torch is present
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m block_wise_kv_amd.build` "
                                "(there is no fallback implementation)")
@@ -196,6 +201,11 @@ def kv_refresh(seq: SeqDesc, mode: str, k_src, v_src, k_cache, v_cache, seq_ids=
     ad = attn_desc(0, k_src.shape[2], k_src.shape[3], _dtype_code(k_src))
     _check(lib().fdllm_kv_refresh(ctypes.byref(seq), ctypes.byref(ad), MODE[mode], _ptr(k_src), _ptr(v_src),
                                   _ptr(k_cache), _ptr(v_cache), _ptr(seq_ids), _ptr(n_seq), _stream(stream)))
+
+
+def set_timing_events(start_event, stop_event):
+    """Arm the measurement hook: the next launch records these hipEvent_t handles (ints)."""
+    _check(lib().fdllm_set_timing_events(start_event, stop_event))
 
 
 def version() -> int:

@@ -191,6 +191,14 @@ fdllm_status fdllm_kv_refresh(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
  * captured in a graph).  bytes must be a multiple of 4. */
 fdllm_status fdllm_workspace_init(void* workspace, size_t bytes, void* stream);
 
+/* Measurement hook for profilers and benchmarks: the next kernel launched by
+ * an fdllm_* call on this host thread records start_event when it begins and
+ * stop_event when it ends (hipExtLaunchKernel), so hipEventElapsedTime gives
+ * the kernel's own duration.  Both are hipEvent_t (as void*) created by the
+ * caller; either may be NULL.  The hook is consumed by that one launch;
+ * (NULL, NULL) disarms it.  Not for use under stream capture. */
+fdllm_status fdllm_set_timing_events(void* start_event, void* stop_event);
+
 const char* fdllm_status_string(int32_t status);
 const char* fdllm_last_error(void);
 int32_t fdllm_version(void);
