@@ -220,12 +220,13 @@ class AttnInputs:
     v_cache: Optional[np.ndarray]
 
 
-def make_attn_inputs(shape: Shape, mode: str, variant: int = 0) -> AttnInputs:
+def make_attn_inputs(shape: Shape, mode: str, variant: int = 0, caches: bool = True) -> AttnInputs:
     """Q, fresh K/V and cached K/V ~ N(0, 1), quantised to the shape's dtype.
 
     The fresh rows are drawn independently of the cache (they stand for the
     block's tokens after some were decoded since the last refresh).
-    ``variant`` selects another independent draw of the same shape.
+    ``variant`` selects another independent draw of the same shape;
+    ``caches=False`` skips drawing the caches.
     """
     s = shape
     cap = s.fresh_capacity(mode)
@@ -233,7 +234,7 @@ def make_attn_inputs(shape: Shape, mode: str, variant: int = 0) -> AttnInputs:
     q = normal((s.batch, cap, s.n_q_heads, s.head_dim), 1.0, s.dtype, *ids, _T_Q)
     kn = normal((s.batch, cap, s.n_kv_heads, s.head_dim), 1.0, s.dtype, *ids, _T_KN)
     vn = normal((s.batch, cap, s.n_kv_heads, s.head_dim), 1.0, s.dtype, *ids, _T_VN)
-    if mode == "none":
+    if mode == "none" or not caches:
         kc = vc = None
     else:
         kc = normal((s.batch, s.n_kv_heads, s.max_seq_len, s.head_dim), 1.0, s.dtype,
