@@ -21,9 +21,10 @@
 //     A operand of O^T += V^T P^T (P in bf16, taken directly from the S^T
 //     accumulator layout, so no shuffle of P is needed).
 // The 4 waves merge (max, sum, O) through LDS.  When the key range is split
-// over several workgroups, each writes an fp32 partial and the last one to
-// arrive (device-scope counter) merges them and writes the output; the
-// counter is reset by that workgroup.
+// over several workgroups, each publishes an fp32 partial with agent-scope
+// (write-through) 16-byte stores and bumps a counter; the last one to arrive
+// reads every partial with agent-scope loads, merges them and writes the
+// output, then resets the counter.
 //
 // Work items are ordered so that the query heads sharing a KV head are
 // adjacent, and the grid is remapped so adjacent items land on the same XCD
@@ -34,6 +35,8 @@
 // row, fp32 throughout.
 #include <float.h>
 #include <stdlib.h>
+
+#include <type_traits>
 
 #include "fdllm_device.h"
 #include "fdllm_internal.h"
@@ -125,6 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_vt_raw[kNW * kD * kVtStride];
   __shared__ float s_m[kNW][kQT], s_l[kNW][kQT];
   __shared__ float s_L[kQT];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lq = lane & 31, hh = lane >> 5;
@@ -178,9 +182,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   uint16_t* vt = s_vt_raw + wid * (kD * kVtStride);
 
-  int kt = g.kb + kKT * wid;
-  load_tile(kt);
-  for (; kt < g.ke; kt += kKT * kNW) {
+  // One 32-key sub-tile; with `prefetch` the next sub-tile's loads are
+  // issued as soon as this one's K and V registers are consumed.  The last
+  // sub-tile of a wave runs without a prefetch (nothing is left to fetch).
+  auto tile_step = [&](int kt, auto prefetch) {
     f32x16 S;
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = 0.f;
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     }
     // K and V of this sub-tile are consumed: fetch the next one while the
     // softmax and the PV product run
-    load_tile(kt + kKT * kNW);
+    if constexpr (decltype(prefetch)::value) load_tile(kt + kKT * kNW);
 
     // lane holds query column lq, keys kt + 8 (r / 4) + 4 hh + (r % 4)
     float mx = -INFINITY;
@@ -265,6 +270,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  int kt = g.kb + kKT * wid;
+  if (kt < g.ke) {
+    load_tile(kt);
+    for (; kt + kKT * kNW < g.ke; kt += kKT * kNW) tile_step(kt, std::true_type{});
+    tile_step(kt, std::false_type{});
   }
 
   // ---- merge the 4 waves (per query column lq)
@@ -286,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   float* red = (float*)s_vt_raw;  // [kNW][kQT][kRedStride], reuses the V tiles
   const bool split = a.n_split > 1;
   const size_t slot = (((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt) * a.n_split + g.s;  // (i, h, qt, s)
-  float* part = split ? a.part + slot * kPartFloats : nullptr;
+  const auto prs = make_rsrc(split ? a.part + slot * kPartFloats : a.part);
   const int oq = tid >> 3;          // query row handled in the output phase
   const int od = 8 * (tid & 7);     // 8 columns within the 64-column half
 
@@ -322,80 +333,72 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
         *(uint4*)(orow + 64 * ph + od) = w;
       }
     } else {
-      float4* dst = (float4*)(part + oq * kD + 64 * ph + od);
-      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+      const int off = (oq * kD + 64 * ph + od) * 4;
+      st_coherent_b128(prs, off, make_float4(o[0], o[1], o[2], o[3]));
+      st_coherent_b128(prs, off + 16, make_float4(o[4], o[5], o[6], o[7]));
     }
     __syncthreads();
   }
-  if (split && wid == 0 && hh == 0) {
-    part[kQT * kD + lq] = M;
-    part[kQT * kD + kQT + lq] = Lsum;
-  }
-}
+  if (!split) return;
 
-// Merge the split-key partials of one (sequence, head, query tile): the
-// second kernel of a split launch, so the partials written with ordinary
-// stores by the first are visible here.  Every partial load is issued
-// before any is used (clamped index, weight 0 past the active splits).
-__global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
-  const int item = blockIdx.x;  // (i, h, qt)
-  const int qt = item % a.n_qt;
-  const int h = (item / a.n_qt) % a.Hq;
-  const int i = item / (a.n_qt * a.Hq);
-  const int P = seq_prompt(a.sq, i);
-  int a0, a1;
-  fresh_range(a.mode, P, a.sq.G, a.sq.B, seq_block(a.sq, i), a0, a1);
-  const int nq = a1 - a0, q0 = qt * kQT;
-  const int tid = threadIdx.x;
+  if (wid == 0 && hh == 0) {
+    st_coherent_b32(prs, (kQT * kD + lq) * 4, M);
+    st_coherent_b32(prs, (kQT * kD + kQT + lq) * 4, Lsum);
+  }
+  uint32_t* cnt = a.cnt + ((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt;
+  if (!block_arrive(cnt, (unsigned)g.n_act, &s_last)) return;
+
+  // ---- last workgroup of this tile: merge the n_act split partials.  Every
+  // partial load is issued before any is used (clamped index, weight 0 past
+  // n_act), so the merge costs one memory round trip.
+  const float* part0 = a.part + (slot - g.s) * kPartFloats;
   const int cq = tid >> 3;            // query row
   const int cd = 16 * (tid & 7);      // 16 columns
-  if (q0 + cq >= nq) return;
-  const int n_act = (P + a.sq.G + a.kchunk - 1) / a.kchunk;
-  const float c = a.scale_log2;
-  const float* part0 = a.part + (size_t)item * a.n_split * kPartFloats;
-  float ms[kMaxSplit], ls[kMaxSplit];
-  float4 xs[kMaxSplit][4];
+  if (q0 + cq < g.nq) {
+    float ms[kMaxSplit], ls[kMaxSplit];
+    float4 xs[kMaxSplit][4];
 #pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s) {
-    const float* ps = part0 + min(s, n_act - 1) * kPartFloats;
-    ms[s] = ps[kQT * kD + cq];
-    ls[s] = ps[kQT * kD + kQT + cq];
+    for (int s = 0; s < kMaxSplit; ++s) {
+      const auto r = make_rsrc(part0 + min(s, g.n_act - 1) * kPartFloats);
+      ms[s] = ld_coherent_b32(r, (kQT * kD + cq) * 4);
+      ls[s] = ld_coherent_b32(r, (kQT * kD + kQT + cq) * 4);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) xs[s][v] = *(const float4*)(ps + cq * kD + cd + 4 * v);
-  }
-  float Mg = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s) Mg = fmaxf(Mg, ms[s]);
-  float wsum = 0.f;
-  float o[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) o[e] = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s) {
-    const float w = (s < n_act) ? exp2_fast((ms[s] - Mg) * c) : 0.f;
-    wsum += ls[s] * w;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      o[4 * v + 0] += xs[s][v].x * w;
-      o[4 * v + 1] += xs[s][v].y * w;
-      o[4 * v + 2] += xs[s][v].z * w;
-      o[4 * v + 3] += xs[s][v].w * w;
+      for (int v = 0; v < 4; ++v) xs[s][v] = ld_coherent_b128(r, (cq * kD + cd + 4 * v) * 4);
     }
+    float Mg = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) Mg = fmaxf(Mg, ms[s]);
+    float wsum = 0.f;
+    float ov[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ov[e] = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) {
+      const float w = (s < g.n_act) ? exp2_fast((ms[s] - Mg) * c) : 0.f;
+      wsum += ls[s] * w;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        ov[4 * v + 0] += xs[s][v].x * w;
+        ov[4 * v + 1] += xs[s][v].y * w;
+        ov[4 * v + 2] += xs[s][v].z * w;
+        ov[4 * v + 3] += xs[s][v].w * w;
+      }
+    }
+    const float inv = 1.f / wsum;
+    uint16_t* orow = (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + cq) * a.Hq + g.h) * kD;
+    uint4 w0, w1;
+    w0.x = pack_bf16x2(ov[0] * inv, ov[1] * inv);
+    w0.y = pack_bf16x2(ov[2] * inv, ov[3] * inv);
+    w0.z = pack_bf16x2(ov[4] * inv, ov[5] * inv);
+    w0.w = pack_bf16x2(ov[6] * inv, ov[7] * inv);
+    w1.x = pack_bf16x2(ov[8] * inv, ov[9] * inv);
+    w1.y = pack_bf16x2(ov[10] * inv, ov[11] * inv);
+    w1.z = pack_bf16x2(ov[12] * inv, ov[13] * inv);
+    w1.w = pack_bf16x2(ov[14] * inv, ov[15] * inv);
+    *(uint4*)(orow + cd) = w0;
+    *(uint4*)(orow + cd + 8) = w1;
   }
-  const float inv = 1.f / wsum;
-  uint16_t* orow = (uint16_t*)a.out + (((size_t)i * a.fresh_rows + q0 + cq) * a.Hq + h) * kD;
-  uint4 w0, w1;
-  w0.x = pack_bf16x2(o[0] * inv, o[1] * inv);
-  w0.y = pack_bf16x2(o[2] * inv, o[3] * inv);
-  w0.z = pack_bf16x2(o[4] * inv, o[5] * inv);
-  w0.w = pack_bf16x2(o[6] * inv, o[7] * inv);
-  w1.x = pack_bf16x2(o[8] * inv, o[9] * inv);
-  w1.y = pack_bf16x2(o[10] * inv, o[11] * inv);
-  w1.z = pack_bf16x2(o[12] * inv, o[13] * inv);
-  w1.w = pack_bf16x2(o[14] * inv, o[15] * inv);
-  *(uint4*)(orow + cd) = w0;
-  *(uint4*)(orow + cd + 8) = w1;
+  if (tid == 0) *cnt = 0u;
 }
 
 // ------------------------------------------------------------------ f32 VALU
@@ -512,7 +515,8 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   p.grid = p.per_xcd * 8;
   if (ns > 1) {
     const size_t slots = (size_t)base * ns;
-    const size_t bytes = slots * kPartFloats * sizeof(float);
+    size_t bytes = slots * kPartFloats * sizeof(float);
+    bytes += (size_t)base * sizeof(uint32_t);  // one counter per (sequence, head, query tile)
     p.ws_bytes = (bytes + 255) & ~(size_t)255;
   }
   return p;
@@ -520,15 +524,8 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
 
 hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, int d, hipStream_t st) {
   const LaunchEvents ev = take_launch_events();
-  if (dtype == 0) {
-    if (p.n_split == 1)
-      return launch_kernel(attn_bf16_kernel, dim3((unsigned)p.grid), dim3(kThreads), 0, st, ev.start, ev.stop, a);
-    hipError_t e = launch_kernel(attn_bf16_kernel, dim3((unsigned)p.grid), dim3(kThreads), 0, st, ev.start,
-                                 (hipEvent_t) nullptr, a);
-    if (e != hipSuccess) return e;
-    const unsigned tiles = (unsigned)(a.sq.b * a.Hq * p.n_qt);
-    return launch_kernel(attn_combine_kernel, dim3(tiles), dim3(kThreads), 0, st, (hipEvent_t) nullptr, ev.stop, a);
-  }
+  if (dtype == 0)
+    return launch_kernel(attn_bf16_kernel, dim3((unsigned)p.grid), dim3(kThreads), 0, st, ev.start, ev.stop, a);
   dim3 grid((unsigned)p.n_qt, (unsigned)a.Hq, (unsigned)a.sq.b);
   return d == 64 ? launch_kernel(attn_f32_kernel<64>, grid, dim3(256), 0, st, ev.start, ev.stop, a)
                  : launch_kernel(attn_f32_kernel<128>, grid, dim3(256), 0, st, ev.start, ev.stop, a);

@@ -153,7 +153,7 @@ fdllm_status setup_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t dtyp
   if (dtype != FDLLM_BF16 && dtype != FDLLM_F32) return fail(FDLLM_ERR_INVALID_ARG, "logits dtype %d invalid", dtype);
   if (seq->block_size > 1024) return fail(FDLLM_ERR_UNSUPPORTED, "block_size > 1024");
   if (seq->batch > 65535) return fail(FDLLM_ERR_UNSUPPORTED, "batch > 65535");
-  if (vocab > 256 * 8192) return fail(FDLLM_ERR_UNSUPPORTED, "vocab > 2097152");
+  if (vocab > (1 << 28)) return fail(FDLLM_ERR_UNSUPPORTED, "vocab > 2^28");
   const UnmaskPlan up = plan_unmask(dtype, vocab, seq->batch * seq->block_size);
   su.chunk = up.chunk;
   su.nchunk = up.nchunk;
@@ -236,6 +236,7 @@ fdllm_status fdllm_block_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
   a.per_xcd = su.plan.per_xcd;
   if (su.plan.ws_bytes > 0) {
     a.part = (float*)workspace;
+    a.cnt = (uint32_t*)((char*)workspace + (size_t)su.plan.n_items * (32 * 128 + 64) * sizeof(float));
   }
   hipError_t e = launch_block_attn(a, su.plan, attn->dtype, attn->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "block_attn launch failed: %s", hipGetErrorString(e));
@@ -293,11 +294,9 @@ fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, in
   const size_t rows = (size_t)seq->batch * seq->block_size;
   char* w = (char*)workspace;
   a.part = (UnmaskPartial*)w;
-  w += (rows * su.nchunk + rows) * sizeof(UnmaskPartial);
+  w += rows * su.nchunk * sizeof(UnmaskPartial);
   a.done_flag = (int32_t*)w;
   w += (size_t)seq->batch * 8;
-  a.row_cnt = (uint32_t*)w;
-  w += rows * 4;
   a.seq_cnt = (uint32_t*)w;
   w += (size_t)seq->batch * 4;
   a.glob_cnt = (uint32_t*)w;

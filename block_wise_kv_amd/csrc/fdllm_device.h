@@ -72,6 +72,27 @@ __device__ __forceinline__ void ld_coherent_f2(const float* p, float& a, float& 
   a = __uint_as_float((uint32_t)w);
   b = __uint_as_float((uint32_t)(w >> 32));
 }
+// 16-byte and 4-byte accesses with the same agent-scope cache policy (sc1),
+// through a raw buffer resource: full-line write-through for bulk partials.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
+}
+constexpr int kCoherentAux = 16;  // sc1
+__device__ __forceinline__ void st_coherent_b128(__amdgpu_buffer_rsrc_t r, int byte_off, float4 v) {
+  u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, byte_off, 0, kCoherentAux);
+}
+__device__ __forceinline__ void st_coherent_b32(__amdgpu_buffer_rsrc_t r, int byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, kCoherentAux);
+}
+__device__ __forceinline__ float4 ld_coherent_b128(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherentAux);
+  return make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
+}
+__device__ __forceinline__ float ld_coherent_b32(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kCoherentAux));
+}
+
 // Wait until this thread's memory operations have completed, then add 1 to
 // the counter; returns the previous count.
 __device__ __forceinline__ unsigned arrive(uint32_t* cnt) {

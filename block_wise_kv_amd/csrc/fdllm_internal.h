@@ -82,9 +82,8 @@ struct UnmaskArgs {
   double* conf;
   int32_t* done_seqs;
   int32_t* n_done;
-  UnmaskPartial* part;      // [b][B][nchunk] chunk partials, then [b][B] row results
+  UnmaskPartial* part;      // [b][B][nchunk] chunk partials
   int32_t* done_flag;       // [b] x 8 bytes
-  uint32_t* row_cnt;        // [b][B]
   uint32_t* seq_cnt;        // [b]
   uint32_t* glob_cnt;       // [1]
   int nchunk;               // vocab chunks per row (one workgroup each)
@@ -112,6 +111,7 @@ struct AttnArgs {
   const void* vc;
   void* out;
   float* part;              // split-key partials [b][Hq][n_qt][n_split] (null when n_split == 1)
+  uint32_t* cnt;            // split-key counters [b][Hq][n_qt]
   int n_qt;                 // query tiles per (sequence, head)
   int n_split;              // key chunks per (sequence, head, query tile)
   int kchunk;               // keys per chunk
