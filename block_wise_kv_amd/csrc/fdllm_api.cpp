@@ -291,15 +291,7 @@ fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, in
   a.n_done = n_done;
   a.nchunk = su.nchunk;
   a.chunk = su.chunk;
-  const size_t rows = (size_t)seq->batch * seq->block_size;
-  char* w = (char*)workspace;
-  a.part = (UnmaskPartial*)w;
-  w += rows * su.nchunk * sizeof(UnmaskPartial);
-  a.done_flag = (int32_t*)w;
-  w += (size_t)seq->batch * 8;
-  a.seq_cnt = (uint32_t*)w;
-  w += (size_t)seq->batch * 4;
-  a.glob_cnt = (uint32_t*)w;
+  unmask_bind_workspace(a, workspace);
   hipError_t e = launch_unmask(a, logits_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "unmask launch failed: %s", hipGetErrorString(e));
   return ok();

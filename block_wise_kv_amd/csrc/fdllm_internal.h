@@ -83,9 +83,9 @@ struct UnmaskArgs {
   int32_t* done_seqs;
   int32_t* n_done;
   UnmaskPartial* part;      // [b][B][nchunk] chunk partials
+  uint64_t* glob;           // [2] finished-sequence counter (and done bits)
   int32_t* done_flag;       // [b] x 8 bytes
   uint32_t* seq_cnt;        // [b]
-  uint32_t* glob_cnt;       // [1]
   int nchunk;               // vocab chunks per row (one workgroup each)
   int chunk;                // vocab entries per chunk (multiple of the vector width)
 };
@@ -94,6 +94,7 @@ struct UnmaskPlan {
 };
 UnmaskPlan plan_unmask(int dtype, int V, int rows);
 size_t unmask_workspace_bytes(int b, int B, int nchunk);
+void unmask_bind_workspace(UnmaskArgs& a, void* workspace);
 hipError_t launch_unmask(const UnmaskArgs& a, int dtype, hipStream_t st);
 
 // ------------------------------------------------------------------ attention

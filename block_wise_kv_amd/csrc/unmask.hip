@@ -12,16 +12,21 @@
 //   1. workgroup (c, t, i) reads vocab chunk c of block row t of sequence i
 //      once from HBM, in iterations of 8 x 16-byte loads per thread; two
 //      register buffers alternate so the next iteration's loads are in
-//      flight while the current one is reduced.  Per thread it keeps the
-//      running max, the iteration where that max first appeared, and the
-//      sum of exp(l - max): one fma and one exp per logit, the exps of an
-//      iteration summed pairwise in fp32 and accumulated in fp64.  The
-//      lowest argmax is located after the chunk, only by the threads whose
-//      max equals the chunk max (one reload of one iteration).
+//      flight while the current one is reduced.  The first two iterations
+//      are requested before the row's mask byte is known, so the mask read
+//      adds no latency (an unmasked row discards them).  Per thread it keeps
+//      the running max, the iteration and load slot where that max first
+//      appeared, and the sum of exp(l - max): one fma and one exp per logit,
+//      the exps of an iteration summed pairwise in fp32 and accumulated in
+//      fp64.  After the chunk every thread re-reads its one slot (in flight
+//      during the workgroup max) and the threads holding the chunk max give
+//      its lowest index.
 //   2. the last workgroup of sequence i to arrive merges every chunk of every
 //      row (fp64), applies the threshold and the fallback with workgroup
 //      reductions, commits tokens and mask, and writes the per-sequence
-//      outputs; the last sequence writes the ascending done list.
+//      outputs; the last sequence writes the ascending done list.  For up to
+//      48 sequences the finished flags ride in the same 64-bit atomic as the
+//      arrival count, so the last sequence reads them from its own atomic.
 // Partials are published with agent-scope write-through stores, a wait for
 // their completion and a relaxed counter atomic, and read back with
 // agent-scope loads: no L2 write-back or invalidate.  Counters are reset by
@@ -42,18 +47,22 @@ constexpr int kUWaves = kUT / 64;
 constexpr int kU = 8;              // 16-byte vectors per thread per iteration
 constexpr int kMaxBlockSize = 1024;
 constexpr int kMaxChunks = 16;     // vocab chunks per row
+constexpr int kBitsSeqs = 48;      // done list carried in one 64-bit atomic up to this batch
 
+// A partial (m, idx, z) is one 16-byte write-through store / load.
 __device__ __forceinline__ void put_partial(UnmaskPartial* p, float m, int idx, double z) {
-  const uint64_t w0 = (uint64_t)__float_as_uint(m) | ((uint64_t)(uint32_t)idx << 32);
-  st_coherent((uint64_t*)p, w0);
-  st_coherent((uint64_t*)p + 1, (uint64_t)__double_as_longlong(z));
+  const uint64_t zb = (uint64_t)__double_as_longlong(z);
+  st_coherent_b128(make_rsrc(p), 0,
+                   make_float4(m, __int_as_float(idx), __uint_as_float((uint32_t)zb),
+                               __uint_as_float((uint32_t)(zb >> 32))));
 }
-__device__ __forceinline__ void get_partial(const UnmaskPartial* p, float& m, int& idx, double& z) {
-  const uint64_t w0 = ld_coherent((const uint64_t*)p);
-  const uint64_t w1 = ld_coherent((const uint64_t*)p + 1);
-  m = __uint_as_float((uint32_t)w0);
-  idx = (int)(uint32_t)(w0 >> 32);
-  z = __longlong_as_double((long long)w1);
+// `r` addresses the sequence's partials (a workgroup-uniform base), `off`
+// is this partial's byte offset from it.
+__device__ __forceinline__ void get_partial(__amdgpu_buffer_rsrc_t r, int off, float& m, int& idx, double& z) {
+  const float4 w = ld_coherent_b128(r, off);
+  m = w.x;
+  idx = __float_as_int(w.y);
+  z = __longlong_as_double((long long)((uint64_t)__float_as_uint(w.z) | ((uint64_t)__float_as_uint(w.w) << 32)));
 }
 
 // ---- logits vectors
@@ -94,27 +103,42 @@ __device__ __forceinline__ float pairwise_sum(float* x) {
   return x[0];
 }
 
-// Running per-thread state: max m, the iteration where m first appeared
-// (-1: none, -2: in the scalar tail, whose index is idx), and
-// z = sum over seen logits of exp(l - m).
+// Running per-thread state: max m, the iteration it and load slot u where m
+// first appeared (it = -1: none, -2: in the scalar tail, whose index is
+// idx), and z = sum over seen logits of exp(l - m).
 struct RowAcc {
   float m;
   int it;
+  int u;
   int idx;
   double z;
 };
 
-// Fold n logits x[0..n) (one iteration) into acc.  The exps use the fp32
-// reference r = round(m*log2 e): exp2(fma(x, log2 e, -r)) = exp(x - m) * 2^d
-// with d = m*log2 e - r computed exactly by one more fma, so the iteration
-// sum is corrected by 2^-d and the maximum contributes (to within an ulp)
-// exactly 1.
-template <int N>
+// Fold one iteration, x[0..N) in S slots of N/S logits (one slot per load,
+// in ascending vocab order), into acc.  The exps use the fp32 reference
+// r = round(m*log2 e): exp2(fma(x, log2 e, -r)) = exp(x - m) * 2^d with
+// d = m*log2 e - r computed exactly by one more fma, so the iteration sum is
+// corrected by 2^-d and the maximum contributes (to within an ulp) exactly 1.
+template <int N, int S>
 __device__ __forceinline__ void fold(RowAcc& acc, float* x, int it) {
-  float lm = -INFINITY;
+  constexpr int E = N / S;
+  float sm[S];
 #pragma unroll
-  for (int k = 0; k < N; ++k) lm = fmaxf(lm, x[k]);
-  if (lm > acc.m) acc.it = it;
+  for (int q = 0; q < S; ++q) {
+    sm[q] = x[q * E];
+#pragma unroll
+    for (int k = 1; k < E; ++k) sm[q] = fmaxf(sm[q], x[q * E + k]);
+  }
+  float lm = sm[0];
+#pragma unroll
+  for (int q = 1; q < S; ++q) lm = fmaxf(lm, sm[q]);
+  int us = 0;
+#pragma unroll
+  for (int q = S - 1; q > 0; --q) us = (sm[q] == lm) ? q : us;
+  if (lm > acc.m) {
+    acc.it = it;
+    acc.u = us;
+  }
   const float m_new = fmaxf(acc.m, lm);
   if (m_new == -INFINITY) return;
   const float r = m_new * kLog2e;
@@ -167,15 +191,17 @@ __device__ __forceinline__ void best_of(double& c, int& t, double c2, int t2) {
 }
 
 // Per-sequence finalisation by the last workgroup of sequence i.  Rows are
-// handled 256 at a time, one per thread; every chunk partial of a row is
-// loaded at once; counts, the fallback argmax and the ranks of selected rows
-// come from workgroup reductions and ballots.
+// handled 256 at a time, one per thread; a row's mask byte and every chunk
+// partial are loaded together (the merge runs on every row and the mask
+// selects); counts, the fallback argmax and the ranks of selected rows come
+// from workgroup reductions and ballots.
 __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
   __shared__ int s_cnt[kUWaves][2];
   __shared__ double s_bc[kUWaves];
   __shared__ int s_bt[kUWaves];
   __shared__ int s_rank[kUWaves];
   __shared__ int s_done, s_count, s_last;
+  __shared__ uint64_t s_bits;
   const int B = a.sq.B;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int32_t* trow = a.tokens + (size_t)i * a.sq.Lcap + start;
@@ -185,6 +211,7 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
   constexpr int kP = kMaxBlockSize / kUT;
 
   // pass 1: per-row confidence, counts and the most confident masked row
+  const __amdgpu_buffer_rsrc_t rpart = make_rsrc(a.part + (size_t)i * B * a.nchunk);
   double conf[kP];
   int tok[kP];
   bool msk[kP];
@@ -197,13 +224,14 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
     msk[p] = false;
     conf[p] = 0.0;
     tok[p] = 0;
-    if (p < np && t < B && mrow[t]) {
-      const UnmaskPartial* pp = a.part + ((size_t)i * B + t) * a.nchunk;
+    if (p < np && t < B) {
+      const bool mk = mrow[t] != 0;
       float mc[kMaxChunks];
       int ic[kMaxChunks];
       double zc[kMaxChunks];
 #pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c) get_partial(pp + min(c, a.nchunk - 1), mc[c], ic[c], zc[c]);
+      for (int c = 0; c < kMaxChunks; ++c)
+        get_partial(rpart, (t * a.nchunk + min(c, a.nchunk - 1)) * (int)sizeof(UnmaskPartial), mc[c], ic[c], zc[c]);
       float M = -INFINITY;
 #pragma unroll
       for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, mc[c]);
@@ -217,10 +245,11 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
           if (mc[c] == M) tk = min(tk, ic[c]);
         }
       }
-      msk[p] = true;
-      conf[p] = 1.0 / Z;
+      // unmasked rows carry stale partials: computed, then discarded
+      msk[p] = mk;
+      conf[p] = mk ? 1.0 / Z : 0.0;
       tok[p] = tk;
-      best_of(bc, bt, conf[p], t);
+      if (mk) best_of(bc, bt, conf[p], t);
     }
     n_masked += msk[p];
     n_pass += msk[p] && conf[p] > tau;
@@ -279,6 +308,8 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
   const int n_sel = base;
   if (a.decoded_pos)
     for (int t = n_sel + tid; t < B; t += kUT) a.decoded_pos[(size_t)i * B + t] = -1;
+  const bool want_list = a.done_seqs || a.n_done;
+  const int b = a.sq.b;
   if (tid == 0) {
     a.n_decoded[i] = n_sel;
     const int done = (n_masked == n_sel) ? 1 : 0;
@@ -289,15 +320,36 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
     a.seq_cnt[i] = 0u;
     s_done = done;
     s_count = 0;
+    if (want_list && b <= kBitsSeqs) {
+      // count in the top 16 bits, finished flags below: adding distinct
+      // bits is an or, so the last arriver holds every flag
+      const uint64_t add = (1ull << 48) | ((uint64_t)done << i);
+      const uint64_t old = __hip_atomic_fetch_add(a.glob, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = (int)(old >> 48) == b - 1;
+      s_bits = (old + add) & ((1ull << 48) - 1ull);
+    }
   }
-  if (!(a.done_seqs || a.n_done)) return;
+  if (!want_list) return;
   // the last sequence to finish writes the ascending list of finished ones
+  if (b <= kBitsSeqs) {
+    __syncthreads();
+    if (!s_last || tid >= 64) return;
+    const bool fl = tid < b && ((s_bits >> tid) & 1ull);
+    const uint64_t bal = __ballot(fl);
+    if (fl && a.done_seqs) a.done_seqs[__popcll(bal & ((1ull << lane) - 1ull))] = tid;
+    if (tid == 0) {
+      if (a.n_done) *a.n_done = __popcll(bal);
+      __hip_atomic_store(a.glob, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  uint32_t* cnt = (uint32_t*)(a.glob + 1);
   __syncthreads();
   if (tid == 0) st_coherent((uint64_t*)(a.done_flag + 2 * i), (uint64_t)s_done);
-  if (!block_arrive(a.glob_cnt, (unsigned)a.sq.b, &s_last)) return;
-  for (int q = 0; q < a.sq.b; q += kUT) {
+  if (!block_arrive(cnt, (unsigned)b, &s_last)) return;
+  for (int q = 0; q < b; q += kUT) {
     const int s = q + tid;
-    const bool fl = s < a.sq.b && ld_coherent((const uint64_t*)(a.done_flag + 2 * s)) != 0;
+    const bool fl = s < b && ld_coherent((const uint64_t*)(a.done_flag + 2 * s)) != 0;
     const uint64_t bal = __ballot(fl);
     const int below = __popcll(bal & ((1ull << lane) - 1ull));
     __syncthreads();
@@ -313,8 +365,19 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
   __syncthreads();
   if (tid == 0) {
     if (a.n_done) *a.n_done = s_count;
-    *a.glob_cnt = 0u;
+    *cnt = 0u;
   }
+}
+
+// A row's mask byte through the scalar cache (its aligned dword, so the
+// read stays in the byte's page).  The kernel writes mask bytes only in the
+// finalisation of a sequence, after every workgroup of that sequence has
+// read its own, so the scalar cache never holds a stale byte.
+__device__ __forceinline__ int load_mask_byte(const uint8_t* p) {
+  typedef const __attribute__((address_space(4))) uint32_t* ConstU32;
+  const uintptr_t addr = (uintptr_t)p;
+  const uint32_t w = *(ConstU32)(addr & ~(uintptr_t)3);
+  return (int)((w >> (8u * (uint32_t)(addr & 3u))) & 0xffu);
 }
 
 template <bool BF16>
@@ -327,102 +390,118 @@ __global__ __launch_bounds__(kUT) void unmask_kernel(UnmaskArgs a) {
   const int tid = threadIdx.x;
   const int B = a.sq.B;
   const int start = seq_prompt(a.sq, i) + seq_block(a.sq, i) * B;
-  const bool masked = a.mask[(size_t)i * a.sq.Lcap + start + t] != 0;
+  const uint8_t* mptr = a.mask + (size_t)i * a.sq.Lcap + start + t;
 
   __shared__ float s_f[kUWaves];
   __shared__ double s_d[kUWaves];
   __shared__ int s_i[kUWaves];
   __shared__ int s_flag;
 
-  if (masked) {
-    const size_t esz = BF16 ? 2 : 4;
-    const char* row = (const char*)a.logits + ((size_t)i * a.seq_stride + (size_t)t * a.row_stride) * esz;
-    const int e0 = c * a.chunk;                      // first vocab id of the chunk
-    const int e1 = min(a.V, e0 + a.chunk);
-    RowAcc acc{-INFINITY, -1, INT_MAX, 0.0};
-    int nfull = 0;                                   // full vectors (vector path)
-    const uint4* rv = (const uint4*)(row + (size_t)e0 * esz);
-    if (a.vec) {
-      nfull = (e1 - e0) / W;
-      const int n_it = (nfull + kIterVec - 1) / kIterVec;
-      // Loads are unconditional (past the chunk they re-read its last vector,
-      // which stays in cache), so the loads in flight are the same on every
-      // path and reducing one buffer never waits for the other.
-      uint4 va[kU], vb[kU];
-      auto load = [&](uint4 (&buf)[kU], int it) {
+  const size_t esz = BF16 ? 2 : 4;
+  const char* row = (const char*)a.logits + ((size_t)i * a.seq_stride + (size_t)t * a.row_stride) * esz;
+  const int e0 = c * a.chunk;                        // first vocab id of the chunk
+  const int e1 = min(a.V, e0 + a.chunk);
+  RowAcc acc{-INFINITY, -1, 0, INT_MAX, 0.0};
+  const int nfull = a.vec ? (e1 - e0) / W : 0;       // full vectors (vector path)
+  // Vector loads are unconditional and clamped to the chunk's last full
+  // vector; a chunk without one (vocab tail shorter than a vector) points
+  // them at the workspace, whose values are never used.
+  const uint4* rv = nfull > 0 ? (const uint4*)(row + (size_t)e0 * esz) : (const uint4*)a.part;
+  const int vlast = max(nfull - 1, 0);
+  bool masked;
+  if (a.vec) {
+    const int n_it = (nfull + kIterVec - 1) / kIterVec;
+    // Past the chunk the loads re-read its last vector, which stays in
+    // cache, so the loads in flight are the same on every path and reducing
+    // one buffer never waits for the other.
+    uint4 va[kU], vb[kU];
+    auto load = [&](uint4 (&buf)[kU], int it) {
 #pragma unroll
-        for (int u = 0; u < kU; ++u) buf[u] = rv[min(it * kIterVec + u * kUT + tid, nfull - 1)];
-      };
-      auto reduce = [&](const uint4 (&buf)[kU], int it) {
-        float x[N];
+      for (int u = 0; u < kU; ++u) buf[u] = rv[min(it * kIterVec + u * kUT + tid, vlast)];
+    };
+    auto reduce = [&](const uint4 (&buf)[kU], int it) {
+      float x[N];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) VT::unpack(buf[u], x + u * W);
-        if ((it + 1) * kIterVec > nfull) {  // the chunk's last, partial iteration
+      for (int u = 0; u < kU; ++u) VT::unpack(buf[u], x + u * W);
+      if ((it + 1) * kIterVec > nfull) {  // the chunk's last, partial iteration
 #pragma unroll
-          for (int u = 0; u < kU; ++u) {
-            const bool ok = it * kIterVec + u * kUT + tid < nfull;
+        for (int u = 0; u < kU; ++u) {
+          const bool ok = it * kIterVec + u * kUT + tid < nfull;
 #pragma unroll
-            for (int e = 0; e < W; ++e) x[u * W + e] = ok ? x[u * W + e] : -INFINITY;
-          }
-        }
-        fold<N>(acc, x, it);
-      };
-      if (n_it > 0) {
-        load(va, 0);
-        for (int it = 0; it < n_it; it += 2) {
-          load(vb, it + 1);
-          reduce(va, it);
-          load(va, it + 2);
-          if (it + 1 < n_it) reduce(vb, it + 1);
+          for (int e = 0; e < W; ++e) x[u * W + e] = ok ? x[u * W + e] : -INFINITY;
         }
       }
-      // vocab entries past the last full vector of the chunk (fewer than W)
-      if (tid == 0) {
-        for (int e = e0 + nfull * W; e < e1; ++e) {
-          float x1[1] = {VT::scalar(row, e)};
-          const float before = acc.m;
-          fold<1>(acc, x1, -2);
-          if (acc.m > before) acc.idx = e;
-        }
-      }
+      fold<N, kU>(acc, x, it);
+    };
+    // The first two iterations are requested before the mask byte is looked
+    // at, and the first runs whatever it says (an unmasked row reduces it and
+    // discards the result), so nothing between these loads and the loop
+    // waits for the mask.
+    if (n_it > 0) {
+      // mask byte first: loads return in order, so it is in before va
+      const int mv = *mptr;
+      __builtin_amdgcn_sched_barrier(0);
+      load(va, 0);
+      load(vb, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      masked = __builtin_amdgcn_readfirstlane(mv) != 0;
+      const int n_run = masked ? n_it : 1;
+      int it = 0;
+      do {
+        reduce(va, it);
+        load(va, it + 2);
+        if (it + 1 < n_run) reduce(vb, it + 1);
+        load(vb, it + 3);
+        it += 2;
+      } while (it < n_run);
     } else {
+      masked = load_mask_byte(mptr) != 0;  // no full vector: only the scalar tail below
+    }
+    // vocab entries past the last full vector of the chunk (fewer than W)
+    if (masked && tid == 0) {
+      for (int e = e0 + nfull * W; e < e1; ++e) {
+        float x1[1] = {VT::scalar(row, e)};
+        const float before = acc.m;
+        fold<1, 1>(acc, x1, -2);
+        if (acc.m > before) acc.idx = e;
+      }
+    }
+  } else {
+    masked = load_mask_byte(mptr) != 0;
+    if (masked) {
       // unaligned rows: one logit per load, same iteration blocking
       for (int it = 0, base = e0; base < e1; ++it, base += N * kUT) {
         float x[N];
 #pragma unroll
         for (int k = 0; k < N; ++k) {
           const int e = base + k * kUT + tid;
-          x[k] = (e < e1) ? VT::scalar(row, e) : -INFINITY;
+          const float v = VT::scalar(row, min(e, e1 - 1));  // unconditional, clamped
+          x[k] = (e < e1) ? v : -INFINITY;
         }
-        fold<N>(acc, x, it);
+        fold<N, N>(acc, x, it);
       }
     }
-    // chunk max, then its lowest index: only threads holding the chunk max
-    // look at the iteration where they first saw it
+  }
+
+  if (masked) {
+    // chunk max, then its lowest index: every thread re-reads the slot where
+    // it first saw its own max (the load overlaps the workgroup max), and
+    // the threads holding the chunk max search it
+    const int vi = min(max(acc.it, 0) * kIterVec + acc.u * kUT + tid, vlast);
+    const uint4 wv = rv[vi];
     const float M = block_max(acc.m, s_f);
     int idx = INT_MAX;
     if (acc.m == M && M != -INFINITY) {
       if (acc.it == -2) {
         idx = acc.idx;
       } else if (a.vec) {
-        for (int u = 0; u < kU && idx == INT_MAX; ++u) {
-          const int vi = acc.it * kIterVec + u * kUT + tid;
-          if (vi < nfull) {
-            float x[W];
-            VT::unpack(rv[vi], x);
-            for (int e = 0; e < W; ++e)
-              if (x[e] == M) {
-                idx = e0 + vi * W + e;
-                break;
-              }
-          }
-        }
+        float x[W];
+        VT::unpack(wv, x);
+#pragma unroll
+        for (int e = W - 1; e >= 0; --e)
+          if (x[e] == M) idx = e0 + vi * W + e;
       } else {
-        const int base = e0 + acc.it * N * kUT;
-        for (int k = 0; k < N && idx == INT_MAX; ++k) {
-          const int e = base + k * kUT + tid;
-          if (e < e1 && VT::scalar(row, e) == M) idx = e;
-        }
+        idx = e0 + (acc.it * N + acc.u) * kUT + tid;
       }
     }
     const double zt = (acc.m == -INFINITY) ? 0.0 : acc.z * (double)exp2_fast((acc.m - M) * kLog2e);
@@ -467,12 +546,26 @@ UnmaskPlan plan_unmask(int dtype, int V, int rows) {
   return p;
 }
 
+// Workspace: chunk partials, the 16-byte finished-sequence counter, then
+// per-sequence done flags and arrival counters.  Zeroed once; every counter
+// is reset by its last user.
 size_t unmask_workspace_bytes(int b, int B, int nchunk) {
   size_t bytes = (size_t)b * B * nchunk * sizeof(UnmaskPartial);  // chunk partials
+  bytes += 16;                                                    // global counter
   bytes += (size_t)b * 8;                                         // done flags
   bytes += (size_t)b * 4;                                         // sequence counters
-  bytes += 16;                                                    // global counter
   return (bytes + 255) & ~(size_t)255;
+}
+
+void unmask_bind_workspace(UnmaskArgs& a, void* workspace) {
+  char* w = (char*)workspace;
+  a.part = (UnmaskPartial*)w;
+  w += (size_t)a.sq.b * a.sq.B * a.nchunk * sizeof(UnmaskPartial);
+  a.glob = (uint64_t*)w;
+  w += 16;
+  a.done_flag = (int32_t*)w;
+  w += (size_t)a.sq.b * 8;
+  a.seq_cnt = (uint32_t*)w;
 }
 
 hipError_t launch_unmask(const UnmaskArgs& a, int dtype, hipStream_t st) {
