@@ -8,28 +8,37 @@
 // the last refresh.  Which rows are fresh depends on the cache mode
 // (none / prefix / DualCache).
 //
-// bf16, d = 128 (MFMA path).  A workgroup of 4 waves owns one (sequence,
-// query head, 32-row query tile, key chunk).  Each wave streams 32-key
-// sub-tiles of the chunk:
-//   * K rows go straight from HBM into MFMA A-operand registers (16-byte
-//     loads; the head dimension is split into 16-byte column pairs, the same
-//     split is used for Q so the contraction over d is unchanged);
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys x queries, fp32);
-//   * online softmax per query column (exp2 with a log2(e) pre-scale);
-//   * V rows are loaded with 16-byte loads, transposed into a wave-private
-//     LDS tile (d-major, 4 keys per 8-byte write), and read back as the
-//     A operand of O^T += V^T P^T (P in bf16, taken directly from the S^T
-//     accumulator layout, so no shuffle of P is needed).
-// The 4 waves merge (max, sum, O) through LDS.  When the key range is split
-// over several workgroups, each publishes an fp32 partial with agent-scope
+// bf16, d = 128 (MFMA path).  A workgroup of 4 waves owns QT query tiles
+// (32 rows each) of one (sequence, KV head) -- the query heads of a GQA
+// group and/or several query tiles of one head -- and one chunk of keys.
+// K/V stream through an LDS ring in 32-key tiles:
+//   * tiles go from HBM straight into LDS (16-byte global_load_lds, no
+//     register staging), several rounds ahead of the compute; every wave
+//     issues its share and waits for its own loads, one barrier per round
+//     makes the round visible to all waves;
+//   * rows are stored row-major with the 16-byte chunks of row r permuted
+//     by an XOR with ((r & 3) << 2 | (r >> 2) & 3), which makes both LDS
+//     read patterns below free of bank conflicts;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows are the A operand
+//     (16-byte LDS reads), Q stays in registers as the B operand;
+//   * online softmax per query column (exp2 with a log2(e) pre-scale; the
+//     accumulator is rescaled only when some column's max grew);
+//   * O^T += V^T P^T: P^T comes straight from the S^T accumulator layout,
+//     and the V^T operand is read with ds_read_b64_tr_b16, which gathers
+//     4 keys x 4 head-dim columns across each 16-lane group, so V never
+//     needs a transposed copy.
+// With QT = 4 every wave owns one query tile and consumes every K/V tile;
+// with QT = 2 or 1 the 2 or 4 waves of a query tile take alternate tiles
+// and merge (max, sum, O) through LDS at the end.  When the keys are split
+// over several workgroups, each publishes fp32 partials with agent-scope
 // (write-through) 16-byte stores and bumps a counter; the last one to arrive
 // reads every partial with agent-scope loads, merges them and writes the
 // output, then resets the counter.
 //
-// Work items are ordered so that the query heads sharing a KV head are
-// adjacent, and the grid is remapped so adjacent items land on the same XCD
-// (workgroups are dealt round-robin over the 8 XCDs): the g heads of a GQA
-// group then read the same K/V rows through one L2.
+// Work items are ordered so that the groups sharing a KV head (and key
+// chunk) are adjacent, and the grid is remapped so adjacent items land on
+// the same XCD (workgroups are dealt round-robin over the 8 XCDs): they
+// then read the same K/V rows through one L2.
 //
 // f32 (any mode, d = 64 or 128): a plain VALU kernel, one wave per query
 // row, fp32 throughout.
@@ -43,15 +52,15 @@
 
 namespace fdllm {
 
-constexpr int kNW = 4;                 // waves per workgroup
-constexpr int kThreads = kNW * 64;
+constexpr int kThreads = 256;          // 4 waves
 constexpr int kQT = 32;                // query rows per tile
-constexpr int kKT = 32;                // keys per wave sub-tile
+constexpr int kKT = 32;                // keys per K/V tile
 constexpr int kD = 128;                // head dim (bf16 path)
-constexpr int kVtStride = 36;          // bf16 per d-row of the transposed V tile
-constexpr int kRedStride = 65;         // floats per query row of the merge buffer
+constexpr int kTileBytes = kKT * kD * 2;         // one K or V tile: 8 KB
 constexpr int kPartFloats = kQT * kD + 2 * kQT;  // one split partial: O, m, l
-constexpr int kMaxSplit = 8;           // key chunks per (sequence, head, query tile)
+constexpr int kMaxSplit = 8;           // key chunks per group
+constexpr int kVtStride = 36;          // bf16 per d-row of the split kernel's transposed V tile
+constexpr int kRedStride = 65;         // floats per query row of the split kernel's merge buffer
 
 struct Geo {
   int i, h, hk, qt, s;
@@ -73,7 +82,7 @@ __device__ __forceinline__ void fresh_range(int mode, int P, int G, int B, int k
 }
 
 // Decode a work item; false if it has nothing to do.
-__device__ __forceinline__ bool decode_item(const AttnArgs& a, int item, Geo& g) {
+__device__ __forceinline__ bool decode_split_item(const AttnArgs& a, int item, Geo& g) {
   int rest = item;
   const int hg = rest % a.g;
   rest /= a.g;
@@ -115,18 +124,88 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
-// ------------------------------------------------------------------ bf16 MFMA
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
+// 16-byte chunk c of K/V tile row r is stored at chunk c ^ ring_swizzle(r).
+__device__ __forceinline__ int ring_swizzle(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// s_waitcnt on the vector-memory counter only (vmcnt <= N), plus lgkmcnt(0)
+// when `lds` is set.
+template <int N, bool LDS>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LDS ? 0 : 15) << 8));
+}
+
+// Workgroup barrier without a memory fence: the ring's hand-offs are
+// ordered by explicit counter waits (a fence here would wait for every load
+// in flight, including the rounds being prefetched).
+__device__ __forceinline__ void ring_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// Four 16-byte LDS reads at addr[i], completed before the block ends (see
+// lds_read_tr16_x8 for why the ring's reads are hidden from the compiler).
+__device__ __forceinline__ void lds_read_b128_x4(const uint32_t* addr, bf16x8* o) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]));
+}
+
+// Eight transpose reads (ds_read_b64_tr_b16) at addr[i] + OFF, completed
+// before the block ends.  The ring's LDS reads are asm blocks with their own
+// wait: the compiler does not see them, so it does not order them after the
+// ring's LDS loads still in flight into other sets (it would wait for every
+// load in flight); the explicit counter waits and barriers of the ring loop
+// order them instead.
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr16_x8(const uint32_t (&addr)[8], short4v (&o)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+        "v"(addr[7]), "i"(OFF));
+}
+
+// ------------------------------------------------------------------ bf16 MFMA, split keys
+// One query tile per workgroup (MHA with a single query tile per head):
+// the 4 waves take alternate 32-key sub-tiles of the workgroup's key chunk,
+// K goes straight from HBM into A-operand registers, V rows are transposed
+// through a wave-private LDS tile, and the next sub-tile's loads are issued
+// as soon as this one's registers are consumed.
+__global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
   // XCD-aware remap: blockIdx.x is dealt round-robin over 8 XCDs; give each
   // XCD a contiguous range of work items.
   const int bid = blockIdx.x;
   const int item = (bid & 7) * a.per_xcd + (bid >> 3);
   if (item >= a.n_items) return;
   Geo g;
-  if (!decode_item(a, item, g)) return;
+  if (!decode_split_item(a, item, g)) return;
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt_raw[kNW * kD * kVtStride];
-  __shared__ float s_m[kNW][kQT], s_l[kNW][kQT];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt_raw[4 * kD * kVtStride];
+  __shared__ float s_m[4][kQT], s_l[4][kQT];
   __shared__ float s_L[kQT];
   __shared__ int s_last;
 
@@ -214,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     }
     // K and V of this sub-tile are consumed: fetch the next one while the
     // softmax and the PV product run
-    if constexpr (decltype(prefetch)::value) load_tile(kt + kKT * kNW);
+    if constexpr (decltype(prefetch)::value) load_tile(kt + kKT * 4);
 
     // lane holds query column lq, keys kt + 8 (r / 4) + 4 hh + (r % 4)
     float mx = -INFINITY;
@@ -274,7 +353,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   int kt = g.kb + kKT * wid;
   if (kt < g.ke) {
     load_tile(kt);
-    for (; kt + kKT * kNW < g.ke; kt += kKT * kNW) tile_step(kt, std::true_type{});
+    for (; kt + kKT * 4 < g.ke; kt += kKT * 4) tile_step(kt, std::true_type{});
     tile_step(kt, std::false_type{});
   }
 
@@ -287,14 +366,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_m[w][lq]);
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][lq]);
   float Lsum = 0.f;
 #pragma unroll
-  for (int w = 0; w < kNW; ++w) Lsum += s_l[w][lq] * exp2_fast((s_m[w][lq] - M) * c);
+  for (int w = 0; w < 4; ++w) Lsum += s_l[w][lq] * exp2_fast((s_m[w][lq] - M) * c);
   const float f = exp2_fast((m_run - M) * c);
   if (wid == 0 && hh == 0) s_L[lq] = Lsum;
 
-  float* red = (float*)s_vt_raw;  // [kNW][kQT][kRedStride], reuses the V tiles
+  float* red = (float*)s_vt_raw;  // [4][kQT][kRedStride], reuses the V tiles
   const bool split = a.n_split > 1;
   const size_t slot = (((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt) * a.n_split + g.s;  // (i, h, qt, s)
   const auto prs = make_rsrc(split ? a.part + slot * kPartFloats : a.part);
@@ -318,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e) {
       float acc = 0.f;
 #pragma unroll
-      for (int w = 0; w < kNW; ++w) acc += red[(w * kQT + oq) * kRedStride + od + e];
+      for (int w = 0; w < 4; ++w) acc += red[(w * kQT + oq) * kRedStride + od + e];
       o[e] = acc;
     }
     if (!split) {
@@ -401,6 +480,469 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   if (tid == 0) *cnt = 0u;
 }
 
+constexpr float kRefSlack = 8.f;       // log2 headroom of the softmax exponent reference
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+// Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+__device__ __forceinline__ float pairwise_sum16(const float* x) {
+  float t[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) t[k] = x[k] + x[k + 8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) t[k] += t[k + 4];
+  return (t[0] + t[2]) + (t[1] + t[3]);
+}
+
+// ------------------------------------------------------------------ bf16 MFMA, LDS ring
+template <int QT, int NR>
+__global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_ring_kernel(AttnArgs a) {
+  constexpr int R = 4 / QT;                         // key tiles per round (one per key phase)
+  constexpr int SET = R * 2 * kTileBytes;           // ring set: R tiles of K then V
+  constexpr int DPR = 4 * R;                        // 1 KB loads per wave per round
+  static_assert(NR >= 3 && NR <= 6, "the pipeline reads two ring sets per round");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NR * SET];
+  __shared__ float s_m[4][kQT], s_l[4][kQT];
+  __shared__ int s_last;
+  auto set_ptr = [&](auto jc) __attribute__((always_inline)) -> uint8_t* {
+    return ring + (decltype(jc)::value % NR) * SET;
+  };
+
+  // XCD-aware remap: blockIdx.x is dealt round-robin over 8 XCDs; give each
+  // XCD a contiguous range of work items.
+  const int bid = blockIdx.x;
+  const int item = (bid & 7) * a.per_xcd + (bid >> 3);
+  if (item >= a.n_items) return;
+  // item = ((i * Hkv + hk) * n_split + s) * n_grp + grp
+  int rest = item;
+  const int grp = rest % a.n_grp;
+  rest /= a.n_grp;
+  const int sp = rest % a.n_split;
+  rest /= a.n_split;
+  Geo g;
+  g.hk = rest % a.Hkv;
+  g.i = rest / a.Hkv;
+  const int P = seq_prompt(a.sq, g.i);
+  g.L = P + a.sq.G;
+  fresh_range(a.mode, P, a.sq.G, a.sq.B, seq_block(a.sq, g.i), g.a0, g.a1);
+  g.nq = g.a1 - g.a0;
+  g.n_act = (g.L + a.kchunk - 1) / a.kchunk;
+  g.kb = sp * a.kchunk;
+  g.ke = min(g.L, g.kb + a.kchunk);
+  if (g.kb >= g.ke) return;                       // chunk past this sequence's keys
+  const int n_live_qt = (g.nq + kQT - 1) / kQT;   // this sequence's query tiles per head
+  if (grp * QT >= a.g * a.n_qt) return;
+  {
+    bool any = false;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int u = grp * QT + t;
+      any |= (u < a.g * a.n_qt) && (u % a.n_qt) < n_live_qt;
+    }
+    if (!any) return;
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lq = lane & 31, hh = lane >> 5;
+  const int qi = wid % QT, ph = wid / QT;
+  const int u = grp * QT + qi;                    // query tile of (i, hk): head-major
+  const int hg = min(u / a.n_qt, a.g - 1);
+  const int qt = u % a.n_qt;
+  const bool live = u < a.g * a.n_qt && qt < n_live_qt;
+  const int h = g.hk * a.g + hg;
+  const int q0 = qt * kQT;
+  const float c = a.scale_log2;
+
+  const uint16_t* knp = (const uint16_t*)a.kn;
+  const uint16_t* vnp = (const uint16_t*)a.vn;
+  const uint16_t* kcp = (const uint16_t*)a.kc;
+  const uint16_t* vcp = (const uint16_t*)a.vc;
+
+  // Q as the B operand of S^T = K Q^T: lane (lq, hh) holds query row lq,
+  // columns [16 ks + 8 hh, +8) for ks = 0..7.  Rows past nq are zero.
+  bf16x8 qop[8];
+  {
+    const int r = q0 + lq;
+    const uint16_t* qrow =
+        (const uint16_t*)a.q + (((size_t)g.i * a.fresh_rows + max(min(r, g.nq - 1), 0)) * a.Hq + h) * kD;
+    const bool rl = live && r < g.nq;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 w = *(const uint4*)(qrow + 16 * ks + 8 * hh);
+      qop[ks] = as_bf16x8(rl ? w : make_uint4(0, 0, 0, 0));
+    }
+  }
+
+  const int n_tiles = (g.ke - g.kb + kKT - 1) / kKT;
+  const int n_rounds = (n_tiles + R - 1) / R;
+
+  // Round q into ring set J: R tiles x (8 KB K + 8 KB V) = 16 R loads of
+  // 1 KB (4 rows each), DPR per wave.  Rows past the chunk re-read its last
+  // row (masked in the softmax), so every round issues the same loads and
+  // the counter waits below are exact.  Load ii4 of a tile covers rows
+  // row_a + 16 (ii4 & 1) of K (ii4 < 2) or V; this lane moves one 16-byte
+  // chunk of it.  A tile that lies wholly in the cache or wholly in the
+  // fresh rows is addressed from a uniform row base plus a fixed lane offset.
+  const int row_a = 4 * wid + (lane >> 4);
+  const int chunk_a = (lane & 15) ^ ring_swizzle(row_a);  // row_a + 16: same swizzle
+  const uint32_t off_c = (uint32_t)(row_a * 256 + 16 * chunk_a);
+  const uint32_t off_f = (uint32_t)(row_a * a.Hkv * 256 + 16 * chunk_a);
+  const size_t fstride = (size_t)a.Hkv * 256;  // bytes between fresh rows of one KV head
+  const char* kc_row0 = (const char*)kcp + ((size_t)g.i * a.Hkv + g.hk) * a.sq.Lcap * 256;
+  const char* vc_row0 = (const char*)vcp + ((size_t)g.i * a.Hkv + g.hk) * a.sq.Lcap * 256;
+  const char* kf_row0 = (const char*)knp + ((size_t)g.i * a.fresh_rows * a.Hkv + g.hk) * 256;
+  const char* vf_row0 = (const char*)vnp + ((size_t)g.i * a.fresh_rows * a.Hkv + g.hk) * 256;
+  auto issue = [&](int q, auto jc) __attribute__((always_inline)) {
+    uint8_t* base = set_ptr(jc);
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho) {
+      uint8_t* dst = base + rho * 2 * kTileBytes + wid * 1024;
+      const int t0 = g.kb + (q * R + rho) * kKT;
+      const bool whole = t0 + kKT <= g.ke;
+      const bool in_cache = whole && (t0 + kKT <= g.a0 || t0 >= g.a1);
+      const bool in_fresh = whole && t0 >= g.a0 && t0 + kKT <= g.a1;
+      if (in_cache || in_fresh) {
+        const char* kt = in_cache ? kc_row0 + (size_t)t0 * 256 : kf_row0 + (size_t)(t0 - g.a0) * fstride;
+        const char* vt = in_cache ? vc_row0 + (size_t)t0 * 256 : vf_row0 + (size_t)(t0 - g.a0) * fstride;
+        const size_t r16 = in_cache ? (size_t)16 * 256 : 16 * fstride;
+        const uint32_t off = in_cache ? off_c : off_f;
+        __builtin_amdgcn_global_load_lds(kt + off, dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kt + r16 + off, dst + 4096, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + off, dst + 8192, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + r16 + off, dst + 12288, 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int ii4 = 0; ii4 < 4; ++ii4) {
+          const int j = min(t0 + row_a + 16 * (ii4 & 1), g.ke - 1);
+          const char* src =
+              (const char*)(ii4 >= 2 ? kv_row(a, vnp, vcp, g, j, kD) : kv_row(a, knp, kcp, g, j, kD)) + 16 * chunk_a;
+          __builtin_amdgcn_global_load_lds(src, dst + ii4 * 4096, 16, 0, 0);
+        }
+      }
+    }
+  };
+
+  f32x16 O[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;  // exponent reference and sum per column
+
+  // V^T operand of key half k2 and head-dim tile dt: element e of lane l is
+  // V[16 k2 + 8 (e / 4) + 4 hh + e % 4][32 dt + lq] (the key order of P^T
+  // below).  In a 16-lane group G the transpose read hands lane
+  // 16 G + 4 a + b element j of the 8 bytes addressed by lane 16 G + 4 j + a
+  // (element b), so lane 16 G + s addresses key 16 k2 + 4 (G / 2) + s / 4
+  // (+ 8 for e >= 4), columns 32 dt + 16 (G % 2) + 4 (s % 4) + [0, 4).
+  // vt_off[2 dt + hi] is that address within the V tile for k2 = 0 (k2 = 1
+  // is 16 rows further, the same swizzle).
+  // K operand of product ks: row lq, 16-byte chunk 2 ks + hh (swizzled).
+  uint32_t k_off[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) k_off[ks] = (uint32_t)(lq * 256 + 16 * ((2 * ks + hh) ^ ring_swizzle(lq)));
+  uint32_t vt_off[8];
+  {
+    const int G = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = 4 * (G >> 1) + (sl >> 2) + 8 * hi;
+        const int col = 32 * dt + 16 * (G & 1) + 4 * (sl & 3);
+        vt_off[2 * dt + hi] = (uint32_t)(r * 256 + 16 * ((col >> 3) ^ ring_swizzle(r)) + 8 * ((col >> 2) & 1));
+      }
+  }
+
+  // S^T of one 32-key tile (K at tb) against this wave's queries.
+  auto stage_s = [&](const uint8_t* tb) __attribute__((always_inline)) -> f32x16 {
+    const uint32_t base = lds_addr(tb);
+    uint32_t ad[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ad[ks] = base + k_off[ks];
+    bf16x8 kop[8];
+    // two accumulation chains, so consecutive products do not wait on each
+    // other; the second half of K is read while the first half multiplies
+    f32x16 S0, S1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S0[r] = S1[r] = 0.f;
+    lds_read_b128_x4(ad, kop);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ks += 2) {
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 1], qop[ks + 1], S1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    lds_read_b128_x4(ad + 4, kop + 4);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 4; ks < 8; ks += 2) {
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 1], qop[ks + 1], S1, 0, 0, 0);
+    }
+    return S0 + S1;
+  };
+
+  // Softmax of S (keys t0..t0+31, V at tb + 8 KB) and O^T += V^T P^T.
+  auto stage_pv = [&](const uint8_t* tb, int t0, f32x16 S) __attribute__((always_inline)) {
+    // V^T operands (see vt_off)
+    bf16x8 vop[2][4];
+    {
+      const uint32_t base = lds_addr(tb);
+      uint32_t ad[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ad[e] = base + vt_off[e];
+      short4v t[8];
+      __builtin_amdgcn_sched_barrier(0);
+      lds_read_tr16_x8<kTileBytes>(ad, t);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        __builtin_memcpy(&vop[0][dt], &t[2 * dt], 8);
+        __builtin_memcpy((char*)&vop[0][dt] + 8, &t[2 * dt + 1], 8);
+      }
+      lds_read_tr16_x8<kTileBytes + 16 * 256>(ad, t);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        __builtin_memcpy(&vop[1][dt], &t[2 * dt], 8);
+        __builtin_memcpy((char*)&vop[1][dt] + 8, &t[2 * dt + 1], 8);
+      }
+    }
+    // lane holds query column lq, keys t0 + 8 (r / 4) + 4 hh + (r % 4)
+    if (t0 + kKT > g.ke) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = t0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key >= g.ke) S[r] = -INFINITY;
+      }
+    }
+    float mx = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // The exponent reference m_ref moves only when some column's max passes
+    // it by more than kRefSlack (log2 units): p <= 2^kRefSlack stays well
+    // inside bf16 and fp32 range, and the accumulator is rarely rescaled.
+    if (__ballot((mx - m_ref) * c > kRefSlack)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = exp2_fast((m_ref - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float mc = m_ref * c;
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = exp2_fast(fmaf(S[r], c, -mc));
+    l_run += pairwise_sum16(p);
+    bf16x8 pop[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      uint4 w;
+      w.x = cvt_pk_bf16(p[8 * h2 + 0], p[8 * h2 + 1]);
+      w.y = cvt_pk_bf16(p[8 * h2 + 2], p[8 * h2 + 3]);
+      w.z = cvt_pk_bf16(p[8 * h2 + 4], p[8 * h2 + 5]);
+      w.w = cvt_pk_bf16(p[8 * h2 + 6], p[8 * h2 + 7]);
+      pop[h2] = as_bf16x8(w);
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[k2][dt], pop[k2], O[dt], 0, 0, 0);
+  };
+
+  // Round q of the ring lives in set q % NR.  Step q: wait until round q+1
+  // is in (rounds q+2.. may stay in flight), barrier, refill the set round
+  // q-1 used, start S^T of this wave's tile of round q+1, then finish the
+  // tile of round q (softmax and P V), whose S^T the previous step started.
+  // The matrix unit runs the next tile's S^T while the vector unit does the
+  // softmax of the current one.
+  f32x16 S_cur;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) S_cur[r] = 0.f;
+  auto step = [&](int q, auto jc) __attribute__((always_inline)) {
+    constexpr int J = decltype(jc)::value;
+    wait_vm<(NR - 3) * DPR, true>();
+    ring_barrier();
+    issue(q + NR - 1, std::integral_constant<int, (J + NR - 1) % NR>{});
+    const int tile_n = (q + 1) * R + ph;
+    f32x16 S_nxt = S_cur;
+    if (live && tile_n < n_tiles) S_nxt = stage_s(set_ptr(std::integral_constant<int, (J + 1) % NR>{}) + ph * 2 * kTileBytes);
+    const int tile = q * R + ph;
+    if (live && tile < n_tiles) stage_pv(set_ptr(jc) + ph * 2 * kTileBytes, g.kb + tile * kKT, S_cur);
+    S_cur = S_nxt;
+  };
+  // Q settles together with round 0 (the first product needs both), before
+  // the later prologue rounds are issued, so no wait for Q is left inside
+  // the loop.
+  issue(0, std::integral_constant<int, 0>{});
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qop[ks]));
+  issue(1, std::integral_constant<int, 1>{});
+  if constexpr (NR > 3) issue(2, std::integral_constant<int, 2>{});
+  if constexpr (NR > 4) issue(3, std::integral_constant<int, 3>{});
+  if constexpr (NR > 5) issue(4, std::integral_constant<int, 4>{});
+  // round 0 in (NR - 2 later rounds in flight): start its S^T
+  wait_vm<(NR - 2) * DPR, true>();
+  ring_barrier();
+  if (live && ph < n_tiles) S_cur = stage_s(ring + ph * 2 * kTileBytes);
+  // steps past the last round only wait, meet at the barrier and refill
+  // (clamped loads): every path through the loop is the same, which keeps
+  // the compiler's view of the loads in flight exact
+  for (int q = 0; q < n_rounds; q += NR) {
+    step(q, std::integral_constant<int, 0>{});
+    step(q + 1, std::integral_constant<int, 1>{});
+    step(q + 2, std::integral_constant<int, 2>{});
+    if constexpr (NR > 3) step(q + 3, std::integral_constant<int, 3>{});
+    if constexpr (NR > 4) step(q + 4, std::integral_constant<int, 4>{});
+    if constexpr (NR > 5) step(q + 5, std::integral_constant<int, 5>{});
+  }
+  // the ring's trailing loads land before its memory is reused
+  wait_vm<0, true>();
+  ring_barrier();
+
+  // ---- combine the R key phases of each query tile (per column lq)
+  const float l_col = l_run + __shfl_xor(l_run, 32, 64);
+  float M = m_ref, Lsum = l_col;
+  if constexpr (R > 1) {
+    if (hh == 0) {
+      s_m[wid][lq] = m_ref;
+      s_l[wid][lq] = l_col;
+    }
+    __syncthreads();
+    M = -INFINITY;
+#pragma unroll
+    for (int p2 = 0; p2 < R; ++p2) M = fmaxf(M, s_m[qi + QT * p2][lq]);
+    Lsum = 0.f;
+#pragma unroll
+    for (int p2 = 0; p2 < R; ++p2) Lsum += s_l[qi + QT * p2][lq] * exp2_fast((s_m[qi + QT * p2][lq] - M) * c);
+    const float f = exp2_fast((m_ref - M) * c);
+    float* red = (float*)ring;  // [(R - 1) QT slots][64 values][64 lanes]
+    if (ph > 0) {
+      float* slot = red + (size_t)((ph - 1) * QT + qi) * 64 * 64;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) slot[(dt * 16 + r) * 64 + lane] = O[dt][r] * f;
+    }
+    __syncthreads();
+    if (ph == 0) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = O[dt][r] * f;
+#pragma unroll
+          for (int p2 = 1; p2 < R; ++p2) v += red[((size_t)((p2 - 1) * QT + qi) * 64 + dt * 16 + r) * 64 + lane];
+          O[dt][r] = v;
+        }
+    }
+  }
+
+  const bool split = a.n_split > 1;
+  const size_t slot = ((((size_t)g.i * a.Hq + h) * a.n_qt + qt) * a.n_split) + sp;  // (i, h, qt, s)
+  if (ph == 0 && live) {
+    if (!split) {
+      // lane holds column q0 + lq, head-dim 32 dt + 8 (r / 4) + 4 hh + [0, 4)
+      if (q0 + lq < g.nq) {
+        const float inv = 1.f / Lsum;
+        uint16_t* orow = (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + lq) * a.Hq + h) * kD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            uint2 w;
+            w.x = pack_bf16x2(O[dt][4 * r4 + 0] * inv, O[dt][4 * r4 + 1] * inv);
+            w.y = pack_bf16x2(O[dt][4 * r4 + 2] * inv, O[dt][4 * r4 + 3] * inv);
+            *(uint2*)(orow + 32 * dt + 8 * r4 + 4 * hh) = w;
+          }
+      }
+    } else {
+      const auto prs = make_rsrc(a.part + slot * kPartFloats);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          st_coherent_b128(prs, (lq * kD + 32 * dt + 8 * r4 + 4 * hh) * 4,
+                           make_float4(O[dt][4 * r4], O[dt][4 * r4 + 1], O[dt][4 * r4 + 2], O[dt][4 * r4 + 3]));
+      if (hh == 0) {
+        st_coherent_b32(prs, (kQT * kD + lq) * 4, M);
+        st_coherent_b32(prs, (kQT * kD + kQT + lq) * 4, Lsum);
+      }
+    }
+  }
+  if (!split) return;
+  uint32_t* cnt = a.cnt + ((size_t)g.i * a.Hkv + g.hk) * a.n_grp + grp;
+  if (!block_arrive(cnt, (unsigned)g.n_act, &s_last)) return;
+
+  // ---- last workgroup of this group: merge the n_act split partials of
+  // each live query tile.  Every partial load of a tile is issued before any
+  // is used (clamped index, weight 0 past n_act): one memory round trip.
+  const int cq = tid >> 3;            // query row
+  const int cd = 16 * (tid & 7);      // 16 columns
+#pragma unroll 1
+  for (int t = 0; t < QT; ++t) {
+    const int ut = grp * QT + t;
+    const int hgt = ut / a.n_qt, qtt = ut % a.n_qt;
+    if (ut >= a.g * a.n_qt || qtt >= n_live_qt) continue;
+    const int ht = g.hk * a.g + hgt;
+    const int q0t = qtt * kQT;
+    if (q0t + cq >= g.nq) continue;
+    const float* part0 = a.part + (((size_t)g.i * a.Hq + ht) * a.n_qt + qtt) * a.n_split * kPartFloats;
+    float ms[kMaxSplit], ls[kMaxSplit];
+    float4 xs[kMaxSplit][4];
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplit; ++s2) {
+      const auto r = make_rsrc(part0 + min(s2, g.n_act - 1) * kPartFloats);
+      ms[s2] = ld_coherent_b32(r, (kQT * kD + cq) * 4);
+      ls[s2] = ld_coherent_b32(r, (kQT * kD + kQT + cq) * 4);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xs[s2][v] = ld_coherent_b128(r, (cq * kD + cd + 4 * v) * 4);
+    }
+    float Mg = -INFINITY;
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplit; ++s2) Mg = fmaxf(Mg, ms[s2]);
+    float wsum = 0.f;
+    float ov[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ov[e] = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplit; ++s2) {
+      const float w = (s2 < g.n_act) ? exp2_fast((ms[s2] - Mg) * c) : 0.f;
+      wsum += ls[s2] * w;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        ov[4 * v + 0] += xs[s2][v].x * w;
+        ov[4 * v + 1] += xs[s2][v].y * w;
+        ov[4 * v + 2] += xs[s2][v].z * w;
+        ov[4 * v + 3] += xs[s2][v].w * w;
+      }
+    }
+    const float inv = 1.f / wsum;
+    uint16_t* orow = (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0t + cq) * a.Hq + ht) * kD;
+    uint4 w0, w1;
+    w0.x = pack_bf16x2(ov[0] * inv, ov[1] * inv);
+    w0.y = pack_bf16x2(ov[2] * inv, ov[3] * inv);
+    w0.z = pack_bf16x2(ov[4] * inv, ov[5] * inv);
+    w0.w = pack_bf16x2(ov[6] * inv, ov[7] * inv);
+    w1.x = pack_bf16x2(ov[8] * inv, ov[9] * inv);
+    w1.y = pack_bf16x2(ov[10] * inv, ov[11] * inv);
+    w1.z = pack_bf16x2(ov[12] * inv, ov[13] * inv);
+    w1.w = pack_bf16x2(ov[14] * inv, ov[15] * inv);
+    *(uint4*)(orow + cd) = w0;
+    *(uint4*)(orow + cd + 8) = w1;
+  }
+  if (tid == 0) *cnt = 0u;
+}
+
 // ------------------------------------------------------------------ f32 VALU
 template <int D>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
@@ -409,8 +951,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const int r = blockIdx.x * 4 + wid;
   Geo g;
   g.i = blockIdx.z;
-  g.h = blockIdx.y;
-  g.hk = g.h / a.g;
+  const int h = blockIdx.y;
+  g.hk = h / a.g;
   const int P = seq_prompt(a.sq, g.i);
   const int k = seq_block(a.sq, g.i);
   g.L = P + a.sq.G;
@@ -419,7 +961,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   __shared__ float s_q[4][D];
   if (r >= g.nq) return;
 
-  const float* qrow = (const float*)a.q + (((size_t)g.i * a.fresh_rows + r) * a.Hq + g.h) * D;
+  const float* qrow = (const float*)a.q + (((size_t)g.i * a.fresh_rows + r) * a.Hq + h) * D;
 #pragma unroll
   for (int u = 0; u < U; ++u) s_q[wid][lane + 64 * u] = qrow[lane + 64 * u];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -465,42 +1007,66 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       for (int u = 0; u < U; ++u) acc[u] = fmaf(pj, vrow[lane + 64 * u], acc[u]);
     }
   }
-  float* orow = (float*)a.out + (((size_t)g.i * a.fresh_rows + r) * a.Hq + g.h) * D;
+  float* orow = (float*)a.out + (((size_t)g.i * a.fresh_rows + r) * a.Hq + h) * D;
   const float inv = 1.f / l;
 #pragma unroll
   for (int u = 0; u < U; ++u) orow[lane + 64 * u] = acc[u] * inv;
 }
 
 // ------------------------------------------------------------------ planning
-// Workgroups the key-split aims for (about two per CU by default; the
-// environment variable FDLLM_ATTN_TARGET_WGS overrides it for tuning).
-static long attn_target_workgroups() {
-  static long v = [] {
-    const char* e = getenv("FDLLM_ATTN_TARGET_WGS");
-    long t = e ? atol(e) : 512;
-    return t > 0 ? t : 512;
-  }();
-  return v;
+static long env_long(const char* name, long dflt) {
+  const char* e = getenv(name);
+  const long v = e ? atol(e) : dflt;
+  return v > 0 ? v : dflt;
 }
 
+static int g_attn_qt = 0, g_attn_wgs = 0;  // fdllm_set_tuning overrides (0: automatic)
+void set_attn_tuning(int qt, int wgs) {
+  g_attn_qt = qt;
+  g_attn_wgs = wgs;
+}
+
+// Kernel and work split (see the choice of QT below).  The key split fills
+// the GPU when there are few work items.  The environment
+// variables FDLLM_ATTN_QT (1: split-key kernel, 2, 4) and
+// FDLLM_ATTN_TARGET_WGS override the defaults for tuning.
 AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max) {
-  (void)Hkv;
   (void)d;
   AttnPlan p{};
   if (dtype != 0) {
     p.n_qt = (nq_max + 3) / 4;
+    p.n_grp = 1;
     p.n_split = 1;
     p.kchunk = L_max;
     p.n_items = b * Hq * p.n_qt;
     p.grid = p.n_qt;
-    p.ws_bytes = 0;
     return p;
   }
+  const int g = Hq / Hkv;
   p.n_qt = (nq_max + kQT - 1) / kQT;
-  const long base = (long)b * Hq * p.n_qt;
-  const int unit = kKT * kNW;  // 128 keys: one sub-tile per wave
+  const int T = g * p.n_qt;  // query tiles per (sequence, KV head)
+  static const long qt_env = env_long("FDLLM_ATTN_QT", 0);
+  int QT = g_attn_qt > 0 ? g_attn_qt : (int)qt_env;
+  // One query tile per head (DualCache): the split-key kernel (sharing K/V
+  // across the heads of a GQA group would need a key split whose merge
+  // costs more than the shared loads save).  Several query tiles per head
+  // (prefix / no cache): the ring, four query tiles per K/V tile.
+  if (QT != 1 && QT != 2 && QT != 4) QT = p.n_qt == 1 ? 1 : (T >= 4 ? 4 : 2);
+  p.qt_per_wg = QT;
+  static const long target_env = env_long("FDLLM_ATTN_TARGET_WGS", 0);
+  long base;
+  int unit;
+  if (QT == 1) {  // split-key kernel: one item per (sequence, query head, query tile, key chunk)
+    p.n_grp = 1;
+    base = (long)b * Hq * p.n_qt;
+    unit = kKT * 4;  // one sub-tile per wave
+  } else {
+    p.n_grp = (T + QT - 1) / QT;
+    base = (long)b * Hkv * p.n_grp;
+    unit = kKT * (4 / QT);  // keys per ring round
+  }
+  const long target = g_attn_wgs > 0 ? g_attn_wgs : target_env > 0 ? target_env : (QT == 4 ? 512 : 256);
   const int max_split = (L_max + unit - 1) / unit;
-  const long target = attn_target_workgroups();
   int ns = (int)((target + base - 1) / base);
   if (ns < 1) ns = 1;
   if (ns > max_split) ns = max_split;
@@ -514,18 +1080,36 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   p.per_xcd = (p.n_items + 7) / 8;
   p.grid = p.per_xcd * 8;
   if (ns > 1) {
-    const size_t slots = (size_t)base * ns;
-    size_t bytes = slots * kPartFloats * sizeof(float);
-    bytes += (size_t)base * sizeof(uint32_t);  // one counter per (sequence, head, query tile)
+    const size_t slots = (size_t)b * Hq * p.n_qt * ns;
+    p.part_bytes = ((slots * kPartFloats * sizeof(float)) + 255) & ~(size_t)255;
+    const size_t counters = QT == 1 ? (size_t)b * Hq * p.n_qt : (size_t)base;
+    const size_t bytes = p.part_bytes + counters * sizeof(uint32_t);
     p.ws_bytes = (bytes + 255) & ~(size_t)255;
   }
   return p;
 }
 
+void attn_bind_workspace(AttnArgs& a, const AttnPlan& p, void* workspace) {
+  a.n_qt = p.n_qt;
+  a.n_grp = p.n_grp;
+  a.n_split = p.n_split;
+  a.kchunk = p.kchunk;
+  a.n_items = p.n_items;
+  a.per_xcd = p.per_xcd;
+  if (p.ws_bytes > 0) {
+    a.part = (float*)workspace;
+    a.cnt = (uint32_t*)((char*)workspace + p.part_bytes);
+  }
+}
+
 hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, int d, hipStream_t st) {
   const LaunchEvents ev = take_launch_events();
-  if (dtype == 0)
-    return launch_kernel(attn_bf16_kernel, dim3((unsigned)p.grid), dim3(kThreads), 0, st, ev.start, ev.stop, a);
+  if (dtype == 0) {
+    const dim3 grid((unsigned)p.grid), block(kThreads);
+    if (p.qt_per_wg == 4) return launch_kernel(attn_ring_kernel<4, 4>, grid, block, 0, st, ev.start, ev.stop, a);
+    if (p.qt_per_wg == 2) return launch_kernel(attn_ring_kernel<2, 4>, grid, block, 0, st, ev.start, ev.stop, a);
+    return launch_kernel(attn_split_kernel, grid, block, 0, st, ev.start, ev.stop, a);
+  }
   dim3 grid((unsigned)p.n_qt, (unsigned)a.Hq, (unsigned)a.sq.b);
   return d == 64 ? launch_kernel(attn_f32_kernel<64>, grid, dim3(256), 0, st, ev.start, ev.stop, a)
                  : launch_kernel(attn_f32_kernel<128>, grid, dim3(256), 0, st, ev.start, ev.stop, a);

@@ -175,6 +175,15 @@ LaunchEvents take_launch_events() {
 
 extern "C" {
 
+fdllm_status fdllm_set_tuning(int32_t attn_qt, int32_t attn_wgs, int32_t unmask_wgs) {
+  if (attn_qt != 0 && attn_qt != 1 && attn_qt != 2 && attn_qt != 4)
+    return fail(FDLLM_ERR_INVALID_ARG, "attn_qt must be 0, 1, 2 or 4 (got %d)", attn_qt);
+  if (attn_wgs < 0 || unmask_wgs < 0) return fail(FDLLM_ERR_INVALID_ARG, "workgroup targets must be >= 0");
+  set_attn_tuning(attn_qt, attn_wgs);
+  set_unmask_tuning(unmask_wgs);
+  return ok();
+}
+
 fdllm_status fdllm_set_timing_events(void* start_event, void* stop_event) {
   g_timing_start = (hipEvent_t)start_event;
   g_timing_stop = (hipEvent_t)stop_event;
@@ -229,15 +238,7 @@ fdllm_status fdllm_block_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
   a.kc = k_cache;
   a.vc = v_cache;
   a.out = out;
-  a.n_qt = su.plan.n_qt;
-  a.n_split = su.plan.n_split;
-  a.kchunk = su.plan.kchunk;
-  a.n_items = su.plan.n_items;
-  a.per_xcd = su.plan.per_xcd;
-  if (su.plan.ws_bytes > 0) {
-    a.part = (float*)workspace;
-    a.cnt = (uint32_t*)((char*)workspace + (size_t)su.plan.n_items * (32 * 128 + 64) * sizeof(float));
-  }
+  attn_bind_workspace(a, su.plan, workspace);
   hipError_t e = launch_block_attn(a, su.plan, attn->dtype, attn->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "block_attn launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -93,6 +93,7 @@ struct UnmaskPlan {
   int nchunk, chunk;
 };
 UnmaskPlan plan_unmask(int dtype, int V, int rows);
+void set_unmask_tuning(int wgs);
 size_t unmask_workspace_bytes(int b, int B, int nchunk);
 void unmask_bind_workspace(UnmaskArgs& a, void* workspace);
 hipError_t launch_unmask(const UnmaskArgs& a, int dtype, hipStream_t st);
@@ -112,19 +113,24 @@ struct AttnArgs {
   const void* vc;
   void* out;
   float* part;              // split-key partials [b][Hq][n_qt][n_split] (null when n_split == 1)
-  uint32_t* cnt;            // split-key counters [b][Hq][n_qt]
-  int n_qt;                 // query tiles per (sequence, head)
-  int n_split;              // key chunks per (sequence, head, query tile)
+  uint32_t* cnt;            // split-key counters [b][Hkv][n_grp]
+  int n_qt;                 // query tiles per (sequence, query head)
+  int n_grp;                // query-tile groups per (sequence, KV head)
+  int n_split;              // key chunks per group
   int kchunk;               // keys per chunk
   int n_items;
   int per_xcd;              // work items per XCD slice of the grid
 };
 
 struct AttnPlan {
-  int n_qt, n_split, kchunk, n_items, per_xcd, grid;
+  int qt_per_wg;            // query tiles sharing each K/V tile in a workgroup (1, 2 or 4)
+  int n_qt, n_grp, n_split, kchunk, n_items, per_xcd, grid;
+  size_t part_bytes;        // split partials at the start of the workspace
   size_t ws_bytes;
 };
 AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max);
+void set_attn_tuning(int qt, int wgs);
+void attn_bind_workspace(AttnArgs& a, const AttnPlan& p, void* workspace);
 hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, int d, hipStream_t st);
 
 // ------------------------------------------------------------------ misc

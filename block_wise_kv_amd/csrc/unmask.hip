@@ -527,13 +527,16 @@ static long unmask_target_workgroups() {
   return v;
 }
 
+static int g_unmask_wgs = 0;  // fdllm_set_tuning override (0: automatic)
+void set_unmask_tuning(int wgs) { g_unmask_wgs = wgs; }
+
 UnmaskPlan plan_unmask(int dtype, int V, int rows) {
   UnmaskPlan p{};
   const int W = dtype == 0 ? 8 : 4;
   const int iter_elems = kU * kUT * W;           // one workgroup iteration
   // split rows so that about the target number of workgroups covers the
   // batch (at most one chunk per iteration and at most 16 chunks per row)
-  const long target = unmask_target_workgroups();
+  const long target = g_unmask_wgs > 0 ? g_unmask_wgs : unmask_target_workgroups();
   const int want = (int)((target + rows - 1) / rows);
   const int by_iter = (V + iter_elems - 1) / iter_elems;
   int nchunk = want < by_iter ? want : by_iter;

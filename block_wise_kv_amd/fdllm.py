@@ -69,6 +69,7 @@ _SIGS = [
      [ctypes.POINTER(SeqDesc), ctypes.POINTER(AttnDesc), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
     ("fdllm_workspace_init", ctypes.c_int32, [_P, ctypes.c_size_t, _P]),
     ("fdllm_set_timing_events", ctypes.c_int32, [_P, _P]),
+    ("fdllm_set_tuning", ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     ("fdllm_status_string", ctypes.c_char_p, [ctypes.c_int32]),
     ("fdllm_last_error", ctypes.c_char_p, []),
     ("fdllm_version", ctypes.c_int32, []),
@@ -206,6 +207,11 @@ def kv_refresh(seq: SeqDesc, mode: str, k_src, v_src, k_cache, v_cache, seq_ids=
 def set_timing_events(start_event, stop_event):
     """Arm the measurement hook: the next launch records these hipEvent_t handles (ints)."""
     _check(lib().fdllm_set_timing_events(start_event, stop_event))
+
+
+def set_tuning(attn_qt: int = 0, attn_wgs: int = 0, unmask_wgs: int = 0):
+    """fdllm_set_tuning: launch-planner overrides (0 = automatic)."""
+    _check(lib().fdllm_set_tuning(int(attn_qt), int(attn_wgs), int(unmask_wgs)))
 
 
 def version() -> int:

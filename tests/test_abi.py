@@ -153,3 +153,21 @@ def test_workspace_init_rejects():
     assert L.fdllm_workspace_init(None, 64, None) == 1
     assert L.fdllm_workspace_init(P1 + 4, 64, None) == 1
     assert L.fdllm_workspace_init(P1, 0, None) == 0
+
+
+def test_set_tuning_rejects_and_replans():
+    import block_wise_kv_amd as fd
+    with pytest.raises(fd.FdllmError):
+        fd.set_tuning(attn_qt=3)
+    with pytest.raises(fd.FdllmError):
+        fd.set_tuning(attn_wgs=-1)
+    seq = fd.seq_desc(8, 2048, 1024, 32, 1024, 0)
+    ad = fd.attn_desc(28, 4, 128, fd.BF16)
+    try:
+        fd.set_tuning(attn_qt=4, attn_wgs=1)
+        one = fd.block_attn_workspace(seq, ad, "dual", 32)
+        fd.set_tuning(attn_qt=4, attn_wgs=4096)
+        many = fd.block_attn_workspace(seq, ad, "dual", 32)
+    finally:
+        fd.set_tuning()
+    assert one == 0 and many > 0  # one key chunk needs no partials

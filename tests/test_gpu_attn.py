@@ -130,3 +130,35 @@ def test_post_refresh_identity_on_gpu():
         outs[mode] = out[:, (a0 - lo):(a0 - lo) + 32]
     assert np.max(np.abs(outs["dual"] - outs["none"])) <= 1e-2
     assert np.max(np.abs(outs["prefix"] - outs["none"])) <= 1e-2
+
+
+VARIANTS = [
+    # name, dtype, b, Hq, Hkv, d, P, G, B, k, mode
+    ("c3like_dual", "bf16", 2, 28, 4, 128, [1024, 1024], 1024, 32, [5, 5], "dual"),
+    ("c3like_prefix", "bf16", 2, 28, 4, 128, [1024, 1024], 1024, 32, [20, 20], "prefix"),
+    ("gqa7_ragged", "bf16", 3, 14, 2, 128, [37, 100, 5], 96, 32, [0, 2, 1], "dual"),
+    ("block4_gqa", "bf16", 2, 8, 2, 128, [13, 40], 16, 4, [3, 0], "dual"),
+    ("none_gqa", "bf16", 2, 6, 3, 128, [17, 70], 32, 16, [0, 1], "none"),
+    ("mha_prefix", "bf16", 2, 4, 4, 128, [130, 64], 160, 32, [1, 2], "prefix"),
+]
+
+
+@pytest.mark.parametrize("wgs", [0, 16, 4096])
+@pytest.mark.parametrize("qt", [1, 2, 4])
+@pytest.mark.parametrize("case", VARIANTS, ids=lambda c: c[0])
+def test_kernel_variants(case, qt, wgs):
+    # every attention kernel (split-key, LDS ring with 2 or 4 query tiles per
+    # workgroup) and key split on the same inputs
+    import block_wise_kv_amd as fd
+    name, dt, b, hq, hkv, d, P, G, B, k, mode = case
+    s = shape_custom(name, dt, b, hq, hkv, d, P, G, B, k, 64, cfg_id=52)
+    inp = make_attn_inputs(s, mode)
+    ragged = not s.uniform
+    say(f"variant {name} qt={qt} wgs={wgs}")
+    fd.set_tuning(attn_qt=qt, attn_wgs=wgs)
+    try:
+        out, outs, _ = run_attn(inp, ragged=ragged, reps=2)
+    finally:
+        fd.set_tuning()
+    check_attn(out, _full(inp), inp, label=f"{name} qt={qt} wgs={wgs}")
+    assert np.array_equal(outs[0], outs[1], equal_nan=True)
