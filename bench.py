@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB between two device buffers 3 times (counter calibration) and exit")
     args = ap.parse_args()
     w = WORKLOADS[args.workload]
     for key in ("steps", "warmup", "layers", "logit_sets"):
@@ -274,8 +276,63 @@ def cpu_baseline(seconds: float):
                       f"in {el:.1f} s, fp64 NumPy oracle, BLAS limited to 1 thread"}
 
 
+def kernel_source_sha256() -> str:
+    """Digest of the HIP sources the counters were taken on (all of csrc/)."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_wise_kv_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by what they read for a plain
+    copy of known size); None when there is no summary for this workload or
+    the kernels have changed since the counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    try:
+        data = json.loads(text[start + 7:end])
+    except ValueError:
+        return None
+    if data.get("source_sha256") != kernel_source_sha256():
+        return None
+    k = data.get("workloads", {}).get(workload, {}).get(kernel)
+    if not k:
+        return None
+    return int(round(k["fetch_kib"] * 1024 * data["fetch_scale"] + k["write_kib"] * 1024 * data["write_scale"]))
+
+
+def copy_probe(mib: int):
+    """A plain device copy of known size, for scaling the HBM byte counters
+    (FETCH_SIZE / WRITE_SIZE) of the profiler: each copy reads and writes
+    exactly `mib` MiB."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "copies": 3}), flush=True)
+
+
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decoding hot path is "
               "measured on a single MI355X and has no multi-GPU mode", file=sys.stderr)
@@ -359,7 +416,8 @@ def main():
         "config": {"workload": b.w["desc"], "name": args.workload, "block_steps_per_step": b.nb,
                    "graph": use_graph, "rotating_sets": {"layers": args.layers, "logits": args.logit_sets}},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dk["GB_per_s"], 1), "peak": 8000.0,
-                     "unit": "GB/s", "frac": round(dk["GB_per_s"] / 8000.0, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(dk["GB_per_s"] / 8000.0, 4),
+                     "traffic": measured_traffic(args.workload, dom), "algorithmic_bytes": dk["bytes"]},
         "kernels": kernels,
         "attn_unmask_block_steps_per_s": round(1.0 / t_au, 1),
     }

@@ -1067,7 +1067,7 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   }
   const long target = g_attn_wgs > 0 ? g_attn_wgs : target_env > 0 ? target_env : (QT == 4 ? 512 : 256);
   const int max_split = (L_max + unit - 1) / unit;
-  int ns = (int)((target + base - 1) / base);
+  int ns = (int)((target + base / 2) / base);  // nearest: one chunk unless the items fall well short
   if (ns < 1) ns = 1;
   if (ns > max_split) ns = max_split;
   if (ns > kMaxSplit) ns = kMaxSplit;

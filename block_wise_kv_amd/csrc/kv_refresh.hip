@@ -16,7 +16,7 @@
 namespace fdllm {
 
 constexpr int kRefreshThreads = 256;
-constexpr int kRefreshVPT = 2;  // vectors of K (and of V) per thread
+constexpr int kRefreshVPT = 4;  // vectors of K (and of V) per thread
 
 __global__ __launch_bounds__(kRefreshThreads) void kv_refresh_kernel(RefreshArgs a) {
   int i = blockIdx.y;
@@ -38,14 +38,15 @@ __global__ __launch_bounds__(kRefreshThreads) void kv_refresh_kernel(RefreshArgs
   u32x4* vd = (u32x4*)a.v_cache + (size_t)i * seq_vecs;
 
   const uint32_t base = blockIdx.x * (kRefreshThreads * kRefreshVPT) + threadIdx.x;
+  if (nvec == 0) return;
+  // loads are unconditional (clamped to the last vector), so all of a
+  // thread's loads are in flight together; only the stores are guarded
   u32x4 kv[kRefreshVPT], vv[kRefreshVPT];
 #pragma unroll
   for (int u = 0; u < kRefreshVPT; ++u) {
-    const uint32_t v = base + u * kRefreshThreads;
-    if (v < nvec) {
-      kv[u] = __builtin_nontemporal_load(ks + v);
-      vv[u] = __builtin_nontemporal_load(vs + v);
-    }
+    const uint32_t v = min(base + u * kRefreshThreads, nvec - 1u);
+    kv[u] = __builtin_nontemporal_load(ks + v);
+    vv[u] = __builtin_nontemporal_load(vs + v);
   }
 #pragma unroll
   for (int u = 0; u < kRefreshVPT; ++u) {
