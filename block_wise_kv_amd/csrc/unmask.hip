@@ -195,6 +195,98 @@ __device__ __forceinline__ void best_of(double& c, int& t, double c2, int t2) {
 // partial are loaded together (the merge runs on every row and the mask
 // selects); counts, the fallback argmax and the ranks of selected rows come
 // from workgroup reductions and ballots.
+// Blocks of up to 64 rows: one wave finalises (one row per lane, counts and
+// ranks from ballots, no workgroup barrier); the finished-sequence atomic is
+// issued as soon as the row count is known, so its round trip overlaps the
+// commit stores.
+__device__ void unmask_finalize_wave(const UnmaskArgs& a, int i, int start) {
+  const int B = a.sq.B;
+  const int t = threadIdx.x;  // lane of wave 0
+  int32_t* trow = a.tokens + (size_t)i * a.sq.Lcap + start;
+  uint8_t* mrow = a.mask + (size_t)i * a.sq.Lcap + start;
+  const double tau = (double)a.tau;
+  const __amdgpu_buffer_rsrc_t rpart = make_rsrc(a.part + (size_t)i * B * a.nchunk);
+  bool mk = false;
+  double conf = 0.0;
+  int tok = 0;
+  if (t < B) {
+    mk = mrow[t] != 0;
+    float mc[kMaxChunks];
+    int ic[kMaxChunks];
+    double zc[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      get_partial(rpart, (t * a.nchunk + min(c, a.nchunk - 1)) * (int)sizeof(UnmaskPartial), mc[c], ic[c], zc[c]);
+    float M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, mc[c]);
+    double Z = 0.0;
+    int tk = INT_MAX;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      if (c < a.nchunk) {
+        Z += zc[c] * (double)exp2_fast((mc[c] - M) * kLog2e);
+        if (mc[c] == M) tk = min(tk, ic[c]);
+      }
+    }
+    conf = mk ? 1.0 / Z : 0.0;
+    tok = tk;
+  }
+  const uint64_t bal_m = __ballot(mk);
+  const uint64_t bal_p = __ballot(mk && conf > tau);
+  const int n_masked = __popcll(bal_m);
+  double bc = mk ? conf : -1.0;
+  int bt = mk ? t : INT_MAX;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) best_of(bc, bt, __shfl_xor(bc, o, 64), __shfl_xor(bt, o, 64));
+  const bool fallback = bal_p == 0 && n_masked > 0;
+  const uint64_t bal_s = fallback ? (bt < 64 ? (1ull << bt) : 0ull) : bal_p;
+  const int n_sel = __popcll(bal_s);
+  const int done = (n_masked == n_sel) ? 1 : 0;
+  const bool want_list = a.done_seqs || a.n_done;
+  const int b = a.sq.b;
+  uint64_t old = 0, add = 0;
+  if (want_list && t == 0) {
+    // count in the top 16 bits, finished flags below: adding distinct bits
+    // is an or, so the last arriver holds every flag
+    add = (1ull << 48) | ((uint64_t)done << i);
+    old = __hip_atomic_fetch_add(a.glob, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const bool sel = (bal_s >> t) & 1ull;
+  if (t < B) {
+    if (sel) {
+      trow[t] = tok;
+      mrow[t] = 0;
+    }
+    if (a.decoded_pos) {
+      // selected rows in ascending order at [0, n_sel), -1 after them
+      if (sel) a.decoded_pos[(size_t)i * B + __popcll(bal_s & ((1ull << t) - 1ull))] = t;
+      if (t >= n_sel) a.decoded_pos[(size_t)i * B + t] = -1;
+    }
+    if (a.conf) a.conf[(size_t)i * B + t] = mk ? conf : __longlong_as_double(0x7ff8000000000000ll);
+  }
+  if (t == 0) {
+    a.n_decoded[i] = n_sel;
+    if ((a.flags & 1u) && done && a.sq.bidx) {
+      const int k = a.sq.bidx[i];
+      if (k + 1 < a.sq.G / a.sq.B) a.sq.bidx[i] = k + 1;
+    }
+    a.seq_cnt[i] = 0u;
+  }
+  if (!want_list) return;
+  // the last sequence to finish writes the ascending list of finished ones
+  const uint64_t old_all = __shfl(old, 0, 64);
+  if ((int)(old_all >> 48) != b - 1) return;
+  const uint64_t bits = (old_all + __shfl(add, 0, 64)) & ((1ull << 48) - 1ull);
+  const bool fl = t < b && ((bits >> t) & 1ull);
+  const uint64_t bal = __ballot(fl);
+  if (fl && a.done_seqs) a.done_seqs[__popcll(bal & ((1ull << t) - 1ull))] = t;
+  if (t == 0) {
+    if (a.n_done) *a.n_done = __popcll(bal);
+    __hip_atomic_store(a.glob, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
   __shared__ int s_cnt[kUWaves][2];
   __shared__ double s_bc[kUWaves];
@@ -513,6 +605,10 @@ __global__ __launch_bounds__(kUT) void unmask_kernel(UnmaskArgs a) {
 
   // the last of the sequence's B x nchunk workgroups finalises it
   if (!block_arrive(&a.seq_cnt[i], (unsigned)(B * a.nchunk), &s_flag)) return;
+  if (B <= 64 && a.sq.b <= kBitsSeqs) {
+    if (tid < 64) unmask_finalize_wave(a, i, start);
+    return;
+  }
   unmask_finalize(a, i, start);
 }
 
