@@ -189,6 +189,66 @@ __device__ __forceinline__ void lds_read_tr16_x8(const uint32_t (&addr)[8], shor
         "v"(addr[7]), "i"(OFF));
 }
 
+// Merge the NS key-chunk partials (O, m, l in fp32) of one query tile, whose
+// partial s starts at float s * kPartFloats of resource r: query row cq,
+// head-dim columns 32 v + 4 j + [0, 4) for v = 0..3, written to orow in bf16.
+// The 8 lanes of a row read one whole 128-byte line per load, and every load
+// is issued before any is used, so the merge costs one memory round trip.
+template <int NS>
+__device__ __forceinline__ void merge_partials_n(__amdgpu_buffer_rsrc_t r, int cq, int j, float c, uint16_t* orow) {
+  float ms[NS], ls[NS];
+  float4 xs[NS][4];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int o = s * kPartFloats;
+    ms[s] = ld_coherent_b32(r, (o + kQT * kD + cq) * 4);
+    ls[s] = ld_coherent_b32(r, (o + kQT * kD + kQT + cq) * 4);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xs[s][v] = ld_coherent_b128(r, (o + cq * kD + 32 * v + 4 * j) * 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float Mg = ms[0];
+#pragma unroll
+  for (int s = 1; s < NS; ++s) Mg = fmaxf(Mg, ms[s]);
+  float wsum = 0.f;
+  float4 ov[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) ov[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float w = exp2_fast((ms[s] - Mg) * c);
+    wsum += ls[s] * w;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      ov[v].x += xs[s][v].x * w;
+      ov[v].y += xs[s][v].y * w;
+      ov[v].z += xs[s][v].z * w;
+      ov[v].w += xs[s][v].w * w;
+    }
+  }
+  const float inv = 1.f / wsum;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    uint2 w;
+    w.x = pack_bf16x2(ov[v].x * inv, ov[v].y * inv);
+    w.y = pack_bf16x2(ov[v].z * inv, ov[v].w * inv);
+    *(uint2*)(orow + 32 * v + 4 * j) = w;
+  }
+}
+// n (wave-uniform, 1..kMaxSplit) partials: only those are read.
+__device__ __forceinline__ void merge_partials(int n, __amdgpu_buffer_rsrc_t r, int cq, int j, float c, uint16_t* orow) {
+  switch (n) {
+    case 1: merge_partials_n<1>(r, cq, j, c, orow); break;
+    case 2: merge_partials_n<2>(r, cq, j, c, orow); break;
+    case 3: merge_partials_n<3>(r, cq, j, c, orow); break;
+    case 4: merge_partials_n<4>(r, cq, j, c, orow); break;
+    case 5: merge_partials_n<5>(r, cq, j, c, orow); break;
+    case 6: merge_partials_n<6>(r, cq, j, c, orow); break;
+    case 7: merge_partials_n<7>(r, cq, j, c, orow); break;
+    default: merge_partials_n<8>(r, cq, j, c, orow); break;
+  }
+}
+
 // ------------------------------------------------------------------ bf16 MFMA, split keys
 // One query tile per workgroup (MHA with a single query tile per head):
 // the 4 waves take alternate 32-key sub-tiles of the workgroup's key chunk,
@@ -378,7 +438,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
   const size_t slot = (((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt) * a.n_split + g.s;  // (i, h, qt, s)
   const auto prs = make_rsrc(split ? a.part + slot * kPartFloats : a.part);
   const int oq = tid >> 3;          // query row handled in the output phase
-  const int od = 8 * (tid & 7);     // 8 columns within the 64-column half
+  // its 8 columns within the 64-column half: contiguous for the bf16 output
+  // (16 bytes per lane), two runs of 4 for the fp32 partial, so that the 8
+  // lanes of a row fill whole 128-byte lines with each store
+  const int c0 = split ? 4 * (tid & 7) : 8 * (tid & 7);
+  const int c1 = c0 + (split ? 32 : 4);
 
 #pragma unroll
   for (int ph = 0; ph < 2; ++ph) {
@@ -395,9 +459,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+      const int col = (e < 4 ? c0 : c1) + (e & 3);
       float acc = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) acc += red[(w * kQT + oq) * kRedStride + od + e];
+      for (int w = 0; w < 4; ++w) acc += red[(w * kQT + oq) * kRedStride + col];
       o[e] = acc;
     }
     if (!split) {
@@ -409,12 +474,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
         w.z = pack_bf16x2(o[4] * inv, o[5] * inv);
         w.w = pack_bf16x2(o[6] * inv, o[7] * inv);
         uint16_t* orow = (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + oq) * a.Hq + g.h) * kD;
-        *(uint4*)(orow + 64 * ph + od) = w;
+        *(uint4*)(orow + 64 * ph + c0) = w;
       }
     } else {
-      const int off = (oq * kD + 64 * ph + od) * 4;
-      st_coherent_b128(prs, off, make_float4(o[0], o[1], o[2], o[3]));
-      st_coherent_b128(prs, off + 16, make_float4(o[4], o[5], o[6], o[7]));
+      st_coherent_b128(prs, (oq * kD + 64 * ph + c0) * 4, make_float4(o[0], o[1], o[2], o[3]));
+      st_coherent_b128(prs, (oq * kD + 64 * ph + c1) * 4, make_float4(o[4], o[5], o[6], o[7]));
     }
     __syncthreads();
   }
@@ -427,56 +491,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
   uint32_t* cnt = a.cnt + ((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt;
   if (!block_arrive(cnt, (unsigned)g.n_act, &s_last)) return;
 
-  // ---- last workgroup of this tile: merge the n_act split partials.  Every
-  // partial load is issued before any is used (clamped index, weight 0 past
-  // n_act), so the merge costs one memory round trip.
-  const float* part0 = a.part + (slot - g.s) * kPartFloats;
+  // ---- last workgroup of this tile: merge the n_act split partials
+  const auto r = make_rsrc(uniform_ptr(a.part + (slot - g.s) * kPartFloats));
   const int cq = tid >> 3;            // query row
-  const int cd = 16 * (tid & 7);      // 16 columns
-  if (q0 + cq < g.nq) {
-    float ms[kMaxSplit], ls[kMaxSplit];
-    float4 xs[kMaxSplit][4];
-#pragma unroll
-    for (int s = 0; s < kMaxSplit; ++s) {
-      const auto r = make_rsrc(part0 + min(s, g.n_act - 1) * kPartFloats);
-      ms[s] = ld_coherent_b32(r, (kQT * kD + cq) * 4);
-      ls[s] = ld_coherent_b32(r, (kQT * kD + kQT + cq) * 4);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) xs[s][v] = ld_coherent_b128(r, (cq * kD + cd + 4 * v) * 4);
-    }
-    float Mg = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kMaxSplit; ++s) Mg = fmaxf(Mg, ms[s]);
-    float wsum = 0.f;
-    float ov[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) ov[e] = 0.f;
-#pragma unroll
-    for (int s = 0; s < kMaxSplit; ++s) {
-      const float w = (s < g.n_act) ? exp2_fast((ms[s] - Mg) * c) : 0.f;
-      wsum += ls[s] * w;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        ov[4 * v + 0] += xs[s][v].x * w;
-        ov[4 * v + 1] += xs[s][v].y * w;
-        ov[4 * v + 2] += xs[s][v].z * w;
-        ov[4 * v + 3] += xs[s][v].w * w;
-      }
-    }
-    const float inv = 1.f / wsum;
-    uint16_t* orow = (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + cq) * a.Hq + g.h) * kD;
-    uint4 w0, w1;
-    w0.x = pack_bf16x2(ov[0] * inv, ov[1] * inv);
-    w0.y = pack_bf16x2(ov[2] * inv, ov[3] * inv);
-    w0.z = pack_bf16x2(ov[4] * inv, ov[5] * inv);
-    w0.w = pack_bf16x2(ov[6] * inv, ov[7] * inv);
-    w1.x = pack_bf16x2(ov[8] * inv, ov[9] * inv);
-    w1.y = pack_bf16x2(ov[10] * inv, ov[11] * inv);
-    w1.z = pack_bf16x2(ov[12] * inv, ov[13] * inv);
-    w1.w = pack_bf16x2(ov[14] * inv, ov[15] * inv);
-    *(uint4*)(orow + cd) = w0;
-    *(uint4*)(orow + cd + 8) = w1;
-  }
+  if (q0 + cq < g.nq)
+    merge_partials(__builtin_amdgcn_readfirstlane(g.n_act), r, cq, tid & 7, c,
+                   (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + cq) * a.Hq + g.h) * kD);
   if (tid == 0) *cnt = 0u;
 }
 
@@ -884,10 +904,8 @@ __global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_r
   if (!block_arrive(cnt, (unsigned)g.n_act, &s_last)) return;
 
   // ---- last workgroup of this group: merge the n_act split partials of
-  // each live query tile.  Every partial load of a tile is issued before any
-  // is used (clamped index, weight 0 past n_act): one memory round trip.
+  // each live query tile
   const int cq = tid >> 3;            // query row
-  const int cd = 16 * (tid & 7);      // 16 columns
 #pragma unroll 1
   for (int t = 0; t < QT; ++t) {
     const int ut = grp * QT + t;
@@ -896,49 +914,9 @@ __global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_r
     const int ht = g.hk * a.g + hgt;
     const int q0t = qtt * kQT;
     if (q0t + cq >= g.nq) continue;
-    const float* part0 = a.part + (((size_t)g.i * a.Hq + ht) * a.n_qt + qtt) * a.n_split * kPartFloats;
-    float ms[kMaxSplit], ls[kMaxSplit];
-    float4 xs[kMaxSplit][4];
-#pragma unroll
-    for (int s2 = 0; s2 < kMaxSplit; ++s2) {
-      const auto r = make_rsrc(part0 + min(s2, g.n_act - 1) * kPartFloats);
-      ms[s2] = ld_coherent_b32(r, (kQT * kD + cq) * 4);
-      ls[s2] = ld_coherent_b32(r, (kQT * kD + kQT + cq) * 4);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) xs[s2][v] = ld_coherent_b128(r, (cq * kD + cd + 4 * v) * 4);
-    }
-    float Mg = -INFINITY;
-#pragma unroll
-    for (int s2 = 0; s2 < kMaxSplit; ++s2) Mg = fmaxf(Mg, ms[s2]);
-    float wsum = 0.f;
-    float ov[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) ov[e] = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < kMaxSplit; ++s2) {
-      const float w = (s2 < g.n_act) ? exp2_fast((ms[s2] - Mg) * c) : 0.f;
-      wsum += ls[s2] * w;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        ov[4 * v + 0] += xs[s2][v].x * w;
-        ov[4 * v + 1] += xs[s2][v].y * w;
-        ov[4 * v + 2] += xs[s2][v].z * w;
-        ov[4 * v + 3] += xs[s2][v].w * w;
-      }
-    }
-    const float inv = 1.f / wsum;
-    uint16_t* orow = (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0t + cq) * a.Hq + ht) * kD;
-    uint4 w0, w1;
-    w0.x = pack_bf16x2(ov[0] * inv, ov[1] * inv);
-    w0.y = pack_bf16x2(ov[2] * inv, ov[3] * inv);
-    w0.z = pack_bf16x2(ov[4] * inv, ov[5] * inv);
-    w0.w = pack_bf16x2(ov[6] * inv, ov[7] * inv);
-    w1.x = pack_bf16x2(ov[8] * inv, ov[9] * inv);
-    w1.y = pack_bf16x2(ov[10] * inv, ov[11] * inv);
-    w1.z = pack_bf16x2(ov[12] * inv, ov[13] * inv);
-    w1.w = pack_bf16x2(ov[14] * inv, ov[15] * inv);
-    *(uint4*)(orow + cd) = w0;
-    *(uint4*)(orow + cd + 8) = w1;
+    const auto r = make_rsrc(uniform_ptr(a.part + (((size_t)g.i * a.Hq + ht) * a.n_qt + qtt) * a.n_split * kPartFloats));
+    merge_partials(__builtin_amdgcn_readfirstlane(g.n_act), r, cq, tid & 7, c,
+                   (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0t + cq) * a.Hq + ht) * kD);
   }
   if (tid == 0) *cnt = 0u;
 }

@@ -77,6 +77,15 @@ __device__ __forceinline__ void ld_coherent_f2(const float* p, float& a, float& 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
 }
+// A pointer the caller knows to be the same in every lane, moved to scalar
+// registers (so that a buffer resource built from it needs no per-lane loop).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 constexpr int kCoherentAux = 16;  // sc1
 __device__ __forceinline__ void st_coherent_b128(__amdgpu_buffer_rsrc_t r, int byte_off, float4 v) {
   u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};

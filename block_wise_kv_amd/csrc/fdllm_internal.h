@@ -82,7 +82,7 @@ struct UnmaskArgs {
   double* conf;
   int32_t* done_seqs;
   int32_t* n_done;
-  UnmaskPartial* part;      // [b][B][nchunk] chunk partials
+  UnmaskPartial* part;      // [b][nchunk][B] chunk partials (a chunk's rows adjacent)
   uint64_t* glob;           // [2] finished-sequence counter (and done bits)
   int32_t* done_flag;       // [b] x 8 bytes
   uint32_t* seq_cnt;        // [b]

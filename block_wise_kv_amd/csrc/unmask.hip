@@ -216,7 +216,7 @@ __device__ void unmask_finalize_wave(const UnmaskArgs& a, int i, int start) {
     double zc[kMaxChunks];
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c)
-      get_partial(rpart, (t * a.nchunk + min(c, a.nchunk - 1)) * (int)sizeof(UnmaskPartial), mc[c], ic[c], zc[c]);
+      get_partial(rpart, (min(c, a.nchunk - 1) * B + t) * (int)sizeof(UnmaskPartial), mc[c], ic[c], zc[c]);
     float M = -INFINITY;
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, mc[c]);
@@ -323,7 +323,7 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
       double zc[kMaxChunks];
 #pragma unroll
       for (int c = 0; c < kMaxChunks; ++c)
-        get_partial(rpart, (t * a.nchunk + min(c, a.nchunk - 1)) * (int)sizeof(UnmaskPartial), mc[c], ic[c], zc[c]);
+        get_partial(rpart, (min(c, a.nchunk - 1) * B + t) * (int)sizeof(UnmaskPartial), mc[c], ic[c], zc[c]);
       float M = -INFINITY;
 #pragma unroll
       for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, mc[c]);
@@ -600,7 +600,7 @@ __global__ __launch_bounds__(kUT) void unmask_kernel(UnmaskArgs a) {
     double Z;
     int I;
     block_sum_min(zt, idx, s_d, s_i, Z, I);
-    if (tid == 0) put_partial(a.part + ((size_t)i * B + t) * a.nchunk + c, M, I, Z);
+    if (tid == 0) put_partial(a.part + ((size_t)i * a.nchunk + c) * B + t, M, I, Z);
   }
 
   // the last of the sequence's B x nchunk workgroups finalises it
