@@ -60,7 +60,12 @@ constexpr int kTileBytes = kKT * kD * 2;         // one K or V tile: 8 KB
 constexpr int kPartFloats = kQT * kD + 2 * kQT;  // one split partial: O, m, l
 constexpr int kMaxSplit = 8;           // key chunks per group
 constexpr int kVtStride = 36;          // bf16 per d-row of the split kernel's transposed V tile
-constexpr int kRedStride = 65;         // floats per query row of the split kernel's merge buffer
+// Split kernel's wave-merge buffer: [4 waves][32 query rows][32 chunks of 4
+// floats]; chunk k of row r sits at k ^ red_swizzle(r), which keeps both the
+// writes (16 rows, one chunk) and the reads (2 rows, 8 chunks) on distinct banks.
+__device__ __forceinline__ int red_swizzle(int r) { return ((r & 1) << 3) | ((r >> 1) & 7); }
+constexpr int kSplitLdsBytes = 4 * kQT * kD * 4;  // also holds the 4 transposed V tiles
+static_assert(kSplitLdsBytes >= 4 * kD * kVtStride * 2, "V tiles fit the merge buffer");
 
 struct Geo {
   int i, h, hk, qt, s;
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
   Geo g;
   if (!decode_split_item(a, item, g)) return;
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt_raw[4 * kD * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt_raw[kSplitLdsBytes / 2];
   __shared__ float s_m[4][kQT], s_l[4][kQT];
   __shared__ float s_L[kQT];
   __shared__ int s_last;
@@ -433,56 +438,57 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
   const float f = exp2_fast((m_run - M) * c);
   if (wid == 0 && hh == 0) s_L[lq] = Lsum;
 
-  float* red = (float*)s_vt_raw;  // [4][kQT][kRedStride], reuses the V tiles
+  // O * f of every wave into the merge buffer (which reuses the V tiles):
+  // lane (lq, hh) holds head dims 32 dt + 8 q + 4 hh + [0, 4), chunk
+  // 8 dt + 2 q + hh of row lq
+  float* red = (float*)s_vt_raw;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = 8 * dt + 2 * q + hh;
+      *(float4*)(red + ((wid * kQT + lq) * 32 + (k ^ red_swizzle(lq))) * 4) =
+          make_float4(O[dt][4 * q] * f, O[dt][4 * q + 1] * f, O[dt][4 * q + 2] * f, O[dt][4 * q + 3] * f);
+    }
+  __syncthreads();
+
+  // thread (oq, j) sums head dims 32 v + 4 j + [0, 4), v = 0..3, of query
+  // row oq over the waves: the 8 lanes of a row cover whole 128-byte lines
   const bool split = a.n_split > 1;
   const size_t slot = (((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt) * a.n_split + g.s;  // (i, h, qt, s)
-  const auto prs = make_rsrc(split ? a.part + slot * kPartFloats : a.part);
-  const int oq = tid >> 3;          // query row handled in the output phase
-  // its 8 columns within the 64-column half: contiguous for the bf16 output
-  // (16 bytes per lane), two runs of 4 for the fp32 partial, so that the 8
-  // lanes of a row fill whole 128-byte lines with each store
-  const int c0 = split ? 4 * (tid & 7) : 8 * (tid & 7);
-  const int c1 = c0 + (split ? 32 : 4);
-
+  const int oq = tid >> 3, oj = tid & 7;
+  float4 o[4];
 #pragma unroll
-  for (int ph = 0; ph < 2; ++ph) {
+  for (int v = 0; v < 4; ++v) {
+    const int k = 8 * v + oj;
+    float4 acc = *(const float4*)(red + (oq * 32 + (k ^ red_swizzle(oq))) * 4);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int dt = 2 * ph + u;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dl = 32 * u + 8 * (r >> 2) + 4 * hh + (r & 3);
-        red[(wid * kQT + lq) * kRedStride + dl] = O[dt][r] * f;
-      }
+    for (int w = 1; w < 4; ++w) {
+      const float4 x = *(const float4*)(red + ((w * kQT + oq) * 32 + (k ^ red_swizzle(oq))) * 4);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
     }
-    __syncthreads();
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int col = (e < 4 ? c0 : c1) + (e & 3);
-      float acc = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) acc += red[(w * kQT + oq) * kRedStride + col];
-      o[e] = acc;
-    }
-    if (!split) {
-      if (q0 + oq < g.nq) {
-        const float inv = 1.f / s_L[oq];
-        uint4 w;
-        w.x = pack_bf16x2(o[0] * inv, o[1] * inv);
-        w.y = pack_bf16x2(o[2] * inv, o[3] * inv);
-        w.z = pack_bf16x2(o[4] * inv, o[5] * inv);
-        w.w = pack_bf16x2(o[6] * inv, o[7] * inv);
-        uint16_t* orow = (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + oq) * a.Hq + g.h) * kD;
-        *(uint4*)(orow + 64 * ph + c0) = w;
-      }
-    } else {
-      st_coherent_b128(prs, (oq * kD + 64 * ph + c0) * 4, make_float4(o[0], o[1], o[2], o[3]));
-      st_coherent_b128(prs, (oq * kD + 64 * ph + c1) * 4, make_float4(o[4], o[5], o[6], o[7]));
-    }
-    __syncthreads();
+    o[v] = acc;
   }
-  if (!split) return;
+  if (!split) {
+    if (q0 + oq < g.nq) {
+      const float inv = 1.f / s_L[oq];
+      uint16_t* orow = (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + oq) * a.Hq + g.h) * kD;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        uint2 w;
+        w.x = pack_bf16x2(o[v].x * inv, o[v].y * inv);
+        w.y = pack_bf16x2(o[v].z * inv, o[v].w * inv);
+        *(uint2*)(orow + 32 * v + 4 * oj) = w;
+      }
+    }
+    return;
+  }
+  const auto prs = make_rsrc(a.part + slot * kPartFloats);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) st_coherent_b128(prs, (oq * kD + 32 * v + 4 * oj) * 4, o[v]);
 
   if (wid == 0 && hh == 0) {
     st_coherent_b32(prs, (kQT * kD + lq) * 4, M);
