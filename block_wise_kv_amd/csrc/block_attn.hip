@@ -196,35 +196,37 @@ __device__ __forceinline__ void lds_read_tr16_x8(const uint32_t (&addr)[8], shor
 
 // Merge the NS key-chunk partials (O, m, l in fp32) of one query tile, whose
 // partial s starts at float s * kPartFloats of resource r: query row cq,
-// head-dim columns 32 v + 4 j + [0, 4) for v = 0..3, written to orow in bf16.
-// The 8 lanes of a row read one whole 128-byte line per load, and every load
-// is issued before any is used, so the merge costs one memory round trip.
-template <int NS>
-__device__ __forceinline__ void merge_partials_n(__amdgpu_buffer_rsrc_t r, int cq, int j, float c, uint16_t* orow) {
+// head-dim columns c0 + 32 v + 4 j + [0, 4) for v = 0..NV-1, written to orow
+// in bf16.  The 8 lanes of a row read one whole 128-byte line per load, and
+// every load is issued before any is used, so the merge costs one memory
+// round trip.
+template <int NS, int NV = 4>
+__device__ __forceinline__ void merge_partials_n(__amdgpu_buffer_rsrc_t r, int cq, int j, float c, uint16_t* orow,
+                                                 int c0 = 0) {
   float ms[NS], ls[NS];
-  float4 xs[NS][4];
+  float4 xs[NS][NV];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int o = s * kPartFloats;
     ms[s] = ld_coherent_b32(r, (o + kQT * kD + cq) * 4);
     ls[s] = ld_coherent_b32(r, (o + kQT * kD + kQT + cq) * 4);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) xs[s][v] = ld_coherent_b128(r, (o + cq * kD + 32 * v + 4 * j) * 4);
+    for (int v = 0; v < NV; ++v) xs[s][v] = ld_coherent_b128(r, (o + cq * kD + c0 + 32 * v + 4 * j) * 4);
   }
   __builtin_amdgcn_sched_barrier(0);
   float Mg = ms[0];
 #pragma unroll
   for (int s = 1; s < NS; ++s) Mg = fmaxf(Mg, ms[s]);
   float wsum = 0.f;
-  float4 ov[4];
+  float4 ov[NV];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) ov[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int v = 0; v < NV; ++v) ov[v] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const float w = exp2_fast((ms[s] - Mg) * c);
     wsum += ls[s] * w;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < NV; ++v) {
       ov[v].x += xs[s][v].x * w;
       ov[v].y += xs[s][v].y * w;
       ov[v].z += xs[s][v].z * w;
@@ -233,11 +235,11 @@ __device__ __forceinline__ void merge_partials_n(__amdgpu_buffer_rsrc_t r, int c
   }
   const float inv = 1.f / wsum;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < NV; ++v) {
     uint2 w;
     w.x = pack_bf16x2(ov[v].x * inv, ov[v].y * inv);
     w.y = pack_bf16x2(ov[v].z * inv, ov[v].w * inv);
-    *(uint2*)(orow + 32 * v + 4 * j) = w;
+    *(uint2*)(orow + c0 + 32 * v + 4 * j) = w;
   }
 }
 // n (wave-uniform, 1..kMaxSplit) partials: only those are read.
@@ -927,6 +929,353 @@ __global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_r
   if (tid == 0) *cnt = 0u;
 }
 
+// ------------------------------------------------------------------ bf16 MFMA, LDS ring, 8 waves
+// The LDS ring above with 8 waves (512 threads) and one K/V tile per round
+// shared by 8 query tiles, one per wave: a GQA group of up to 8 heads with
+// one query tile each (DualCache) reads every K/V tile once for all its
+// heads, and two waves per SIMD hide each other's latency.  Every wave
+// moves 2 of a tile's 16 loads of 1 KB.  Split partials are stored with
+// plain whole-line stores and merged by attn_merge_kernel (one launch
+// later), so no workgroup has to read a whole group's partials.
+constexpr int kGqaWaves = 8;
+constexpr int kGqaThreads = 64 * kGqaWaves;
+template <int NR>
+__global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
+  constexpr int QPW = kGqaWaves;                    // query tiles per workgroup
+  constexpr int SET = 2 * kTileBytes;               // ring set: one tile of K then V
+  constexpr int DPR = 2;                            // 1 KB loads per wave per round
+  static_assert(NR >= 4 && NR <= 6, "the pipeline reads two ring sets per round; the epilogue needs 64 KB");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NR * SET];
+  auto set_ptr = [&](auto jc) __attribute__((always_inline)) -> uint8_t* {
+    return ring + (decltype(jc)::value % NR) * SET;
+  };
+
+  const int bid = blockIdx.x;
+  const int item = (bid & 7) * a.per_xcd + (bid >> 3);
+  if (item >= a.n_items) return;
+  // item = ((i * Hkv + hk) * n_split + s) * n_grp + grp
+  int rest = item;
+  const int grp = rest % a.n_grp;
+  rest /= a.n_grp;
+  const int sp = rest % a.n_split;
+  rest /= a.n_split;
+  Geo g;
+  g.hk = rest % a.Hkv;
+  g.i = rest / a.Hkv;
+  const int P = seq_prompt(a.sq, g.i);
+  g.L = P + a.sq.G;
+  fresh_range(a.mode, P, a.sq.G, a.sq.B, seq_block(a.sq, g.i), g.a0, g.a1);
+  g.nq = g.a1 - g.a0;
+  g.kb = sp * a.kchunk;
+  g.ke = min(g.L, g.kb + a.kchunk);
+  if (g.kb >= g.ke) return;                       // chunk past this sequence's keys
+  const int T = a.g * a.n_qt;                     // query tiles of (i, hk), head-major
+  const int n_live_qt = (g.nq + kQT - 1) / kQT;
+  {
+    bool any = false;
+    for (int u = grp * QPW; u < min(T, grp * QPW + QPW); ++u) any |= (u % a.n_qt) < n_live_qt;
+    if (!any) return;
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lq = lane & 31, hh = lane >> 5;
+  const int u = grp * QPW + wid;                  // this wave's query tile
+  const int qt = u % a.n_qt;
+  const bool live = u < T && qt < n_live_qt;
+  const int h = g.hk * a.g + min(u / a.n_qt, a.g - 1);
+  const int q0 = qt * kQT;
+  const float c = a.scale_log2;
+
+  const uint16_t* knp = (const uint16_t*)a.kn;
+  const uint16_t* vnp = (const uint16_t*)a.vn;
+  const uint16_t* kcp = (const uint16_t*)a.kc;
+  const uint16_t* vcp = (const uint16_t*)a.vc;
+
+  // Q as the B operand of S^T = K Q^T: lane (lq, hh) holds query row lq,
+  // columns [16 ks + 8 hh, +8) for ks = 0..7.  Rows past nq are zero.
+  bf16x8 qop[8];
+  {
+    const int r = q0 + lq;
+    const uint16_t* qrow =
+        (const uint16_t*)a.q + (((size_t)g.i * a.fresh_rows + max(min(r, g.nq - 1), 0)) * a.Hq + h) * kD;
+    const bool rl = live && r < g.nq;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 w = *(const uint4*)(qrow + 16 * ks + 8 * hh);
+      qop[ks] = as_bf16x8(rl ? w : make_uint4(0, 0, 0, 0));
+    }
+  }
+
+  const int n_tiles = (g.ke - g.kb + kKT - 1) / kKT;
+
+  // Tile q into ring set J: wave w moves rows 4 w + [0, 4) of K and of V
+  // (one 1 KB load each); this lane moves one 16-byte chunk, the one that
+  // belongs at its LDS position under the ring swizzle.  Rows past the
+  // chunk re-read its last row (masked in the softmax), so every round
+  // issues the same loads and the counter waits below are exact.
+  const int row_a = 4 * wid + (lane >> 4);
+  const int chunk_a = (lane & 15) ^ ring_swizzle(row_a);
+  const uint32_t off_c = (uint32_t)(row_a * 256 + 16 * chunk_a);
+  const uint32_t off_f = (uint32_t)(row_a * a.Hkv * 256 + 16 * chunk_a);
+  const size_t fstride = (size_t)a.Hkv * 256;
+  const char* kc_row0 = (const char*)kcp + ((size_t)g.i * a.Hkv + g.hk) * a.sq.Lcap * 256;
+  const char* vc_row0 = (const char*)vcp + ((size_t)g.i * a.Hkv + g.hk) * a.sq.Lcap * 256;
+  const char* kf_row0 = (const char*)knp + ((size_t)g.i * a.fresh_rows * a.Hkv + g.hk) * 256;
+  const char* vf_row0 = (const char*)vnp + ((size_t)g.i * a.fresh_rows * a.Hkv + g.hk) * 256;
+  auto issue = [&](int q, auto jc) __attribute__((always_inline)) {
+    uint8_t* dst = set_ptr(jc) + wid * 1024;
+    const int t0 = g.kb + q * kKT;
+    const bool whole = t0 + kKT <= g.ke;
+    const bool in_cache = whole && (t0 + kKT <= g.a0 || t0 >= g.a1);
+    const bool in_fresh = whole && t0 >= g.a0 && t0 + kKT <= g.a1;
+    if (in_cache || in_fresh) {
+      const char* kt = in_cache ? kc_row0 + (size_t)t0 * 256 : kf_row0 + (size_t)(t0 - g.a0) * fstride;
+      const char* vt = in_cache ? vc_row0 + (size_t)t0 * 256 : vf_row0 + (size_t)(t0 - g.a0) * fstride;
+      const uint32_t off = in_cache ? off_c : off_f;
+      __builtin_amdgcn_global_load_lds(kt + off, dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vt + off, dst + kTileBytes, 16, 0, 0);
+    } else {
+      const int j = min(t0 + row_a, g.ke - 1);
+      __builtin_amdgcn_global_load_lds((const char*)kv_row(a, knp, kcp, g, j, kD) + 16 * chunk_a, dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const char*)kv_row(a, vnp, vcp, g, j, kD) + 16 * chunk_a, dst + kTileBytes, 16,
+                                       0, 0);
+    }
+  };
+
+  f32x16 O[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;  // exponent reference and sum per column
+
+  // operand addresses within a tile (as in the LDS ring kernel)
+  uint32_t k_off[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) k_off[ks] = (uint32_t)(lq * 256 + 16 * ((2 * ks + hh) ^ ring_swizzle(lq)));
+  uint32_t vt_off[8];
+  {
+    const int G = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = 4 * (G >> 1) + (sl >> 2) + 8 * hi;
+        const int col = 32 * dt + 16 * (G & 1) + 4 * (sl & 3);
+        vt_off[2 * dt + hi] = (uint32_t)(r * 256 + 16 * ((col >> 3) ^ ring_swizzle(r)) + 8 * ((col >> 2) & 1));
+      }
+  }
+
+  auto stage_s = [&](const uint8_t* tb) __attribute__((always_inline)) -> f32x16 {
+    const uint32_t base = lds_addr(tb);
+    uint32_t ad[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ad[ks] = base + k_off[ks];
+    bf16x8 kop[8];
+    f32x16 S0, S1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S0[r] = S1[r] = 0.f;
+    lds_read_b128_x4(ad, kop);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ks += 2) {
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 1], qop[ks + 1], S1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    lds_read_b128_x4(ad + 4, kop + 4);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 4; ks < 8; ks += 2) {
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 1], qop[ks + 1], S1, 0, 0, 0);
+    }
+    return S0 + S1;
+  };
+
+  auto stage_pv = [&](const uint8_t* tb, int t0, f32x16 S) __attribute__((always_inline)) {
+    bf16x8 vop[2][4];
+    {
+      const uint32_t base = lds_addr(tb);
+      uint32_t ad[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ad[e] = base + vt_off[e];
+      short4v tr[8];
+      __builtin_amdgcn_sched_barrier(0);
+      lds_read_tr16_x8<kTileBytes>(ad, tr);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        __builtin_memcpy(&vop[0][dt], &tr[2 * dt], 8);
+        __builtin_memcpy((char*)&vop[0][dt] + 8, &tr[2 * dt + 1], 8);
+      }
+      lds_read_tr16_x8<kTileBytes + 16 * 256>(ad, tr);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        __builtin_memcpy(&vop[1][dt], &tr[2 * dt], 8);
+        __builtin_memcpy((char*)&vop[1][dt] + 8, &tr[2 * dt + 1], 8);
+      }
+    }
+    if (t0 + kKT > g.ke) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = t0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key >= g.ke) S[r] = -INFINITY;
+      }
+    }
+    float mx = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (__ballot((mx - m_ref) * c > kRefSlack)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = exp2_fast((m_ref - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float mc = m_ref * c;
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = exp2_fast(fmaf(S[r], c, -mc));
+    l_run += pairwise_sum16(p);
+    bf16x8 pop[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      uint4 w;
+      w.x = cvt_pk_bf16(p[8 * h2 + 0], p[8 * h2 + 1]);
+      w.y = cvt_pk_bf16(p[8 * h2 + 2], p[8 * h2 + 3]);
+      w.z = cvt_pk_bf16(p[8 * h2 + 4], p[8 * h2 + 5]);
+      w.w = cvt_pk_bf16(p[8 * h2 + 6], p[8 * h2 + 7]);
+      pop[h2] = as_bf16x8(w);
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[k2][dt], pop[k2], O[dt], 0, 0, 0);
+  };
+
+  // the LDS ring kernel's pipeline with one tile per round: step q waits
+  // until tile q + 1 is in, meets at the barrier, refills the set tile
+  // q - 1 used, starts S^T of tile q + 1 and finishes tile q
+  f32x16 S_cur;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) S_cur[r] = 0.f;
+  auto step = [&](int q, auto jc) __attribute__((always_inline)) {
+    constexpr int J = decltype(jc)::value;
+    wait_vm<(NR - 3) * DPR, true>();
+    ring_barrier();
+    issue(q + NR - 1, std::integral_constant<int, (J + NR - 1) % NR>{});
+    f32x16 S_nxt = S_cur;
+    if (live && q + 1 < n_tiles) S_nxt = stage_s(set_ptr(std::integral_constant<int, (J + 1) % NR>{}));
+    if (live && q < n_tiles) stage_pv(set_ptr(jc), g.kb + q * kKT, S_cur);
+    S_cur = S_nxt;
+  };
+  issue(0, std::integral_constant<int, 0>{});
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qop[ks]));
+  issue(1, std::integral_constant<int, 1>{});
+  issue(2, std::integral_constant<int, 2>{});
+  if constexpr (NR > 4) issue(3, std::integral_constant<int, 3>{});
+  if constexpr (NR > 5) issue(4, std::integral_constant<int, 4>{});
+  wait_vm<(NR - 2) * DPR, true>();
+  ring_barrier();
+  if (live) S_cur = stage_s(ring);
+  for (int q = 0; q < n_tiles; q += NR) {
+    step(q, std::integral_constant<int, 0>{});
+    step(q + 1, std::integral_constant<int, 1>{});
+    step(q + 2, std::integral_constant<int, 2>{});
+    step(q + 3, std::integral_constant<int, 3>{});
+    if constexpr (NR > 4) step(q + 4, std::integral_constant<int, 4>{});
+    if constexpr (NR > 5) step(q + 5, std::integral_constant<int, 5>{});
+  }
+  wait_vm<0, true>();
+  ring_barrier();
+  if (!live) return;
+
+  const float l_col = l_run + __shfl_xor(l_run, 32, 64);
+  if (a.n_split == 1) {
+    // lane holds column q0 + lq, head-dim 32 dt + 8 (r / 4) + 4 hh + [0, 4)
+    if (q0 + lq < g.nq) {
+      const float inv = 1.f / l_col;
+      uint16_t* orow = (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + lq) * a.Hq + h) * kD;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          uint2 w;
+          w.x = pack_bf16x2(O[dt][4 * r4 + 0] * inv, O[dt][4 * r4 + 1] * inv);
+          w.y = pack_bf16x2(O[dt][4 * r4 + 2] * inv, O[dt][4 * r4 + 3] * inv);
+          *(uint2*)(orow + 32 * dt + 8 * r4 + 4 * hh) = w;
+        }
+    }
+    return;
+  }
+  // Partial (O, m, l) relative to the tile's exponent reference.  O goes
+  // through 8 KB of LDS per wave, 16 head dims at a time (row lq, chunk
+  // 2 q + hh of the 8 in the half, at chunk ^ (lq & 7)), so that each global
+  // store writes 4 whole 256-byte rows... of the half: 4 x 128 bytes.
+  float* part = a.part + ((((size_t)g.i * a.Hq + h) * a.n_qt + qt) * a.n_split + sp) * kPartFloats;
+  float* wbuf = (float*)(ring + wid * 8192);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    // head dims 64 hf + [0, 64): dt = 2 hf + dd
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int k = 8 * dd + 2 * q4 + hh;  // chunk of 4 floats within the 64-dim half
+        const int dt = 2 * hf + dd;
+        *(float4*)(wbuf + (lq * 16 + (k ^ (lq & 15))) * 4) =
+            make_float4(O[dt][4 * q4], O[dt][4 * q4 + 1], O[dt][4 * q4 + 2], O[dt][4 * q4 + 3]);
+      }
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int row = 4 * v + (lane >> 4), k = lane & 15;
+      *(float4*)(part + row * kD + 64 * hf + 4 * k) = *(const float4*)(wbuf + (row * 16 + (k ^ (row & 15))) * 4);
+    }
+  }
+  if (hh == 0) {
+    part[kQT * kD + lq] = m_ref;
+    part[kQT * kD + kQT + lq] = l_col;
+  }
+}
+
+// Merge the key-chunk partials written by attn_gqa_kernel in the launch
+// before: workgroup (query tile x 4 + column quarter, query head, sequence)
+// merges 32 head-dim columns of the tile's 32 rows, so the partial reads
+// spread over four times as many workgroups as query tiles.
+__global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
+  const int qt = blockIdx.x >> 2, quarter = blockIdx.x & 3, h = blockIdx.y, i = blockIdx.z;
+  const int P = seq_prompt(a.sq, i);
+  const int L = P + a.sq.G;
+  int a0, a1;
+  fresh_range(a.mode, P, a.sq.G, a.sq.B, seq_block(a.sq, i), a0, a1);
+  const int nq = a1 - a0;
+  const int q0 = qt * kQT;
+  if (q0 >= nq) return;
+  const int n_act = __builtin_amdgcn_readfirstlane((L + a.kchunk - 1) / a.kchunk);
+  const auto r = make_rsrc(uniform_ptr(a.part + (((size_t)i * a.Hq + h) * a.n_qt + qt) * a.n_split * kPartFloats));
+  const int tid = threadIdx.x;
+  const int cq = tid >> 3, j = tid & 7, c0 = 32 * quarter;
+  if (q0 + cq >= nq) return;
+  uint16_t* orow = (uint16_t*)a.out + (((size_t)i * a.fresh_rows + q0 + cq) * a.Hq + h) * kD;
+  const float c = a.scale_log2;
+  switch (n_act) {
+    case 1: merge_partials_n<1, 1>(r, cq, j, c, orow, c0); break;
+    case 2: merge_partials_n<2, 1>(r, cq, j, c, orow, c0); break;
+    case 3: merge_partials_n<3, 1>(r, cq, j, c, orow, c0); break;
+    case 4: merge_partials_n<4, 1>(r, cq, j, c, orow, c0); break;
+    case 5: merge_partials_n<5, 1>(r, cq, j, c, orow, c0); break;
+    case 6: merge_partials_n<6, 1>(r, cq, j, c, orow, c0); break;
+    case 7: merge_partials_n<7, 1>(r, cq, j, c, orow, c0); break;
+    default: merge_partials_n<8, 1>(r, cq, j, c, orow, c0); break;
+  }
+}
+
 // ------------------------------------------------------------------ f32 VALU
 template <int D>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
@@ -1012,8 +1361,9 @@ void set_attn_tuning(int qt, int wgs) {
 
 // Kernel and work split (see the choice of QT below).  The key split fills
 // the GPU when there are few work items.  The environment
-// variables FDLLM_ATTN_QT (1: split-key kernel, 2, 4) and
-// FDLLM_ATTN_TARGET_WGS override the defaults for tuning.
+// variables FDLLM_ATTN_QT (1: split-key kernel, 2, 4: LDS ring, 8: LDS ring
+// with two query tiles per wave) and FDLLM_ATTN_TARGET_WGS override the
+// defaults for tuning.
 AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max) {
   (void)d;
   AttnPlan p{};
@@ -1035,7 +1385,10 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   // across the heads of a GQA group would need a key split whose merge
   // costs more than the shared loads save).  Several query tiles per head
   // (prefix / no cache): the ring, four query tiles per K/V tile.
-  if (QT != 1 && QT != 2 && QT != 4) QT = p.n_qt == 1 ? 1 : (T >= 4 ? 4 : 2);
+  // A GQA group of 4 or more heads with one query tile each: the ring with
+  // two query tiles per wave (8 per workgroup), so the group's heads share
+  // every K/V tile.
+  if (QT != 1 && QT != 2 && QT != 4 && QT != 8) QT = p.n_qt == 1 ? (g >= 4 ? 8 : 1) : (T >= 4 ? 4 : 2);
   p.qt_per_wg = QT;
   static const long target_env = env_long("FDLLM_ATTN_TARGET_WGS", 0);
   long base;
@@ -1044,6 +1397,10 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
     p.n_grp = 1;
     base = (long)b * Hq * p.n_qt;
     unit = kKT * 4;  // one sub-tile per wave
+  } else if (QT == 8) {
+    p.n_grp = (T + 7) / 8;
+    base = (long)b * Hkv * p.n_grp;
+    unit = kKT;  // one tile per ring round
   } else {
     p.n_grp = (T + QT - 1) / QT;
     base = (long)b * Hkv * p.n_grp;
@@ -1066,7 +1423,9 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   if (ns > 1) {
     const size_t slots = (size_t)b * Hq * p.n_qt * ns;
     p.part_bytes = ((slots * kPartFloats * sizeof(float)) + 255) & ~(size_t)255;
-    const size_t counters = QT == 1 ? (size_t)b * Hq * p.n_qt : (size_t)base;
+    // arrival counters for the in-kernel merge (the 8-tile ring is merged by
+    // a second kernel and needs none)
+    const size_t counters = QT == 1 ? (size_t)b * Hq * p.n_qt : QT == 8 ? 0 : (size_t)base;
     const size_t bytes = p.part_bytes + counters * sizeof(uint32_t);
     p.ws_bytes = (bytes + 255) & ~(size_t)255;
   }
@@ -1090,6 +1449,15 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, in
   const LaunchEvents ev = take_launch_events();
   if (dtype == 0) {
     const dim3 grid((unsigned)p.grid), block(kThreads);
+    if (p.qt_per_wg == 8) {
+      auto* kern = attn_gqa_kernel<4>;
+      const dim3 gblock(kGqaThreads);
+      if (p.n_split == 1) return launch_kernel(kern, grid, gblock, 0, st, ev.start, ev.stop, a);
+      const hipError_t e = launch_kernel(kern, grid, gblock, 0, st, ev.start, (hipEvent_t) nullptr, a);
+      if (e != hipSuccess) return e;
+      const dim3 mgrid((unsigned)p.n_qt * 4, (unsigned)a.Hq, (unsigned)a.sq.b);
+      return launch_kernel(attn_merge_kernel, mgrid, block, 0, st, (hipEvent_t) nullptr, ev.stop, a);
+    }
     if (p.qt_per_wg == 4) return launch_kernel(attn_ring_kernel<4, 4>, grid, block, 0, st, ev.start, ev.stop, a);
     if (p.qt_per_wg == 2) return launch_kernel(attn_ring_kernel<2, 4>, grid, block, 0, st, ev.start, ev.stop, a);
     return launch_kernel(attn_split_kernel, grid, block, 0, st, ev.start, ev.stop, a);

@@ -205,13 +205,15 @@ fdllm_status fdllm_set_timing_events(void* start_event, void* stop_event);
  * FDLLM_UNMASK_TARGET_WGS also override).
  *   attn_qt     1: split-key attention kernel (one query tile per
  *               workgroup, bf16); 2 or 4: LDS-ring kernel with that many
- *               query tiles of one KV head per workgroup.
+ *               query tiles of one KV head per workgroup; 8: LDS ring with
+ *               two query tiles per wave (8 per workgroup), key-chunk
+ *               partials merged by a second kernel in the same call.
  *   attn_wgs    workgroups the attention key split aims for (>= 0).
  *   unmask_wgs  workgroups the unmask vocab split aims for (>= 0).
  * Process-wide; the workspace sizes reported afterwards follow the new
  * plan, so query them again before the next call.  Not safe against
  * concurrent launches from other threads.  FDLLM_ERR_INVALID_ARG for an
- * attn_qt outside {0, 1, 2, 4} or a negative target. */
+ * attn_qt outside {0, 1, 2, 4, 8} or a negative target. */
 fdllm_status fdllm_set_tuning(int32_t attn_qt, int32_t attn_wgs, int32_t unmask_wgs);
 
 const char* fdllm_status_string(int32_t status);

@@ -168,6 +168,12 @@ def test_set_tuning_rejects_and_replans():
         one = fd.block_attn_workspace(seq, ad, "dual", 32)
         fd.set_tuning(attn_qt=4, attn_wgs=4096)
         many = fd.block_attn_workspace(seq, ad, "dual", 32)
+        fd.set_tuning(attn_qt=8, attn_wgs=1)
+        one8 = fd.block_attn_workspace(seq, ad, "dual", 32)
+        fd.set_tuning(attn_qt=8)
+        auto8 = fd.block_attn_workspace(seq, ad, "dual", 32)
     finally:
         fd.set_tuning()
     assert one == 0 and many > 0  # one key chunk needs no partials
+    # 8 key chunks of fp32 partials (O, m, l per row) for 8 x 28 heads x 32 rows
+    assert one8 == 0 and auto8 == 8 * 28 * 8 * (32 * 128 + 64) * 4

@@ -144,11 +144,11 @@ VARIANTS = [
 
 
 @pytest.mark.parametrize("wgs", [0, 16, 4096])
-@pytest.mark.parametrize("qt", [1, 2, 4])
+@pytest.mark.parametrize("qt", [1, 2, 4, 8])
 @pytest.mark.parametrize("case", VARIANTS, ids=lambda c: c[0])
 def test_kernel_variants(case, qt, wgs):
     # every attention kernel (split-key, LDS ring with 2 or 4 query tiles per
-    # workgroup) and key split on the same inputs
+    # workgroup, LDS ring with 2 per wave) and key split on the same inputs
     import block_wise_kv_amd as fd
     name, dt, b, hq, hkv, d, P, G, B, k, mode = case
     s = shape_custom(name, dt, b, hq, hkv, d, P, G, B, k, 64, cfg_id=52)
