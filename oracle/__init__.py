@@ -21,6 +21,13 @@ Parity status of each function (pins live in tests/test_oracle_*.py):
                         monotonicity, hand-computed golden fixture)
 * ``refresh_ref``       pinned (bit-exact copy, sentinel, idempotence, subset)
 * ``decode_block_ref``  pinned (step counts 1..m, tau>=1 -> m steps)
+* ``unmask_topk_ref``   pinned (k >= m -> whole block, k = 1 -> the
+                        threshold rule's single-best fallback, top-k == the
+                        threshold rule at a threshold between the k-th and
+                        (k+1)-th confidence, brute-force ordering over all
+                        masks of a small block, unread rows)
+* ``tokens_per_step``   pinned (the pages' own flag settings)
+* ``decode_block_topk_ref`` pinned (ceil(m / k) steps of k tokens)
 * model-level quality (accuracy, real staleness drift, Theorem 1):
   parity unpinned -- needs trained weights and datasets, out of scope.
 """
@@ -32,5 +39,8 @@ from .fdllm_oracle import (  # noqa: F401
     UnmaskResult,
     refresh_ref,
     decode_block_ref,
+    unmask_topk_ref,
+    tokens_per_step,
+    decode_block_topk_ref,
     NEAR_TIE,
 )

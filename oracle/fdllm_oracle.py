@@ -240,6 +240,83 @@ def unmask_ref(logits, tokens, mask, prompt_lens, gen_len: int, block_size: int,
                         t_tau, t_top2, t_step)
 
 
+def unmask_topk_ref(logits, tokens, mask, prompt_lens, gen_len: int, block_size: int,
+                    block_idxs, k: int, advance: bool = False) -> UnmaskResult:
+    """One fixed-step unmasking step: decode the k most confident masked rows.
+
+    [README] section "Usage": the sampling-steps flag fixes the number of
+    denoising steps, so a fixed number of tokens is committed per step (gen
+    length / steps; one per step with the defaults).  This is the decoding
+    the pages use as their baseline ("LLaDA" and "+cache" columns of the
+    evaluation table).  Which positions are committed is not on the pages;
+    read here as the min(k, m) masked positions of the current block with
+    the highest confidence (the same max-probability confidence as the
+    threshold rule), the lower block offset first among equal confidences.
+    The committed token is the row's argmax, as in the threshold rule.
+
+    Near ties: tie_top2 as in unmask_ref; tie_step marks a sequence whose
+    k-th and (k+1)-th largest confidences are within NEAR_TIE (the chosen set
+    hinges on that comparison); tie_tau and fallback are always False.
+    """
+    if int(k) < 1:
+        raise ValueError("k must be >= 1")
+    tokens = np.array(tokens, np.int32, copy=True)
+    mask = np.array(mask, np.uint8, copy=True)
+    bidx = np.array(block_idxs, np.int32, copy=True).reshape(-1)
+    b = tokens.shape[0]
+    B = block_size
+    n_dec = np.zeros(b, np.int32)
+    dpos = np.full((b, B), -1, np.int32)
+    conf = np.full((b, B), np.nan)
+    done = np.zeros(b, bool)
+    t_top2 = np.zeros((b, B), bool)
+    t_step = np.zeros(b, bool)
+    n_blocks = gen_len // B
+    for i in range(b):
+        start = int(prompt_lens[i]) + int(bidx[i]) * B
+        masked = [t for t in range(B) if mask[i, start + t] == 1]
+        tok = {}
+        for t in masked:
+            c, v, _, _ = row_confidence(logits[i][t])
+            conf[i, t] = c
+            tok[t] = v
+            srt = np.sort(np.asarray(logits[i][t], np.float64))
+            t_top2[i, t] = srt.size > 1 and (srt[-1] - srt[-2]) <= NEAR_TIE
+        # rank the masked rows: higher confidence first, lower offset first
+        order = sorted(masked, key=lambda t: (-conf[i, t], t))
+        chosen = order[:int(k)]
+        if len(order) > int(k) and conf[i, order[int(k) - 1]] - conf[i, order[int(k)]] <= NEAR_TIE:
+            t_step[i] = True
+        for t in chosen:
+            tokens[i, start + t] = tok[t]
+            mask[i, start + t] = 0
+        chosen.sort()
+        n_dec[i] = len(chosen)
+        dpos[i, :len(chosen)] = chosen
+        done[i] = not any(mask[i, start + t] == 1 for t in range(B))
+        if advance and done[i] and bidx[i] + 1 < n_blocks:
+            bidx[i] += 1
+    done_seqs = np.array([i for i in range(b) if done[i]], np.int32)
+    z = np.zeros((b, B), bool)
+    return UnmaskResult(tokens, mask, n_dec, dpos, conf, done, done_seqs, bidx,
+                        np.zeros(b, bool), z, t_top2, t_step)
+
+
+def tokens_per_step(gen_len: int, block_size: int, steps: int) -> int:
+    """Tokens committed per step by the fixed-step schedule.
+
+    [README] "Usage": steps sampling steps over a generation of gen_len
+    tokens decoded block by block.  Read as steps / (gen_len / block_size)
+    steps per block, each committing the same number of tokens; the pages'
+    own settings (gen 128 / steps 128, gen 64 / steps 64, block 32) divide
+    evenly, and uneven schedules are rejected rather than guessed.
+    """
+    n_blocks = gen_len // block_size
+    if gen_len % block_size or steps % n_blocks or block_size % (steps // n_blocks):
+        raise ValueError("steps must split evenly over the blocks and the block over its steps")
+    return block_size // (steps // n_blocks)
+
+
 # ---------------------------------------------------------------------------
 # (c) cache refresh at a block boundary
 # ---------------------------------------------------------------------------
@@ -296,6 +373,25 @@ def decode_block_ref(logits_for_step: Callable[[int], np.ndarray], tokens, mask,
     for step in range(max_steps):
         r = unmask_ref(logits_for_step(step), tokens, mask, prompt_lens, gen_len,
                        block_size, block_idxs, threshold)
+        tokens, mask = r.tokens, r.mask
+        per_step.append(r.n_decoded)
+        if r.done.all():
+            return per_step
+    raise RuntimeError("block did not finish")
+
+
+def decode_block_topk_ref(logits_for_step: Callable[[int], np.ndarray], tokens, mask,
+                          prompt_lens, gen_len: int, block_size: int, block_idxs,
+                          k: int, max_steps: int = 10_000) -> List[np.ndarray]:
+    """The fixed-step loop: k tokens per step until the block is decoded.
+
+    Same loop as decode_block_ref with the top-k step; returns the per-step
+    n_decoded arrays.
+    """
+    per_step = []
+    for step in range(max_steps):
+        r = unmask_topk_ref(logits_for_step(step), tokens, mask, prompt_lens, gen_len,
+                            block_size, block_idxs, k)
         tokens, mask = r.tokens, r.mask
         per_step.append(r.n_decoded)
         if r.done.all():
