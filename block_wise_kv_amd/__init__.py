@@ -6,5 +6,6 @@ include/fdllm.h); this package holds the ctypes binding and the build step.
 from .fdllm import (  # noqa: F401
     BF16, F32, MODE, UNMASK_ADVANCE_BLOCK, FdllmError, SeqDesc, AttnDesc,
     attn_desc, block_attn, block_attn_workspace, kv_refresh, lib, new_workspace,
-    seq_desc, set_timing_events, set_tuning, unmask_threshold, unmask_workspace, version, workspace_init,
+    seq_desc, set_timing_events, set_tuning, unmask_threshold, unmask_topk, unmask_workspace, version,
+    workspace_init,
 )

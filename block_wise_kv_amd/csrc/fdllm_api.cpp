@@ -250,17 +250,21 @@ size_t fdllm_unmask_workspace(const fdllm_seq_desc* seq, int32_t vocab, int32_t 
   return su.ws;
 }
 
-fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype,
-                                    const void* logits, int64_t seq_stride, int64_t row_stride, float threshold,
-                                    uint32_t flags, int32_t* tokens, uint8_t* mask, int32_t* n_decoded,
-                                    int32_t* decoded_pos, double* conf, int32_t* done_seqs, int32_t* n_done,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The threshold rule (topk == 0) and the fixed-step rule (topk > 0) share
+// the vocabulary pass and differ only in the selection of the finalisation.
+fdllm_status run_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype, const void* logits,
+                        int64_t seq_stride, int64_t row_stride, float threshold, int32_t topk, uint32_t flags,
+                        int32_t* tokens, uint8_t* mask, int32_t* n_decoded, int32_t* decoded_pos, double* conf,
+                        int32_t* done_seqs, int32_t* n_done, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   UnmaskSetup su;
   fdllm_status st = setup_unmask(seq, vocab, logits_dtype, su);
   if (st) return st;
   if (!logits || !tokens || !mask || !n_decoded)
     return fail(FDLLM_ERR_INVALID_ARG, "logits, tokens, mask and n_decoded must be non-NULL");
-  if (isnan(threshold)) return fail(FDLLM_ERR_INVALID_ARG, "threshold is NaN");
   if (flags & ~FDLLM_UNMASK_ADVANCE_BLOCK) return fail(FDLLM_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if ((flags & FDLLM_UNMASK_ADVANCE_BLOCK) && !seq->block_idxs)
     return fail(FDLLM_ERR_INVALID_ARG, "FDLLM_UNMASK_ADVANCE_BLOCK needs a device block_idxs array");
@@ -282,6 +286,7 @@ fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, in
   a.logits = logits;
   a.vec = vec ? 1 : 0;
   a.tau = threshold;
+  a.topk = topk;
   a.flags = flags;
   a.tokens = tokens;
   a.mask = mask;
@@ -296,6 +301,29 @@ fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, in
   hipError_t e = launch_unmask(a, logits_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "unmask launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype,
+                                    const void* logits, int64_t seq_stride, int64_t row_stride, float threshold,
+                                    uint32_t flags, int32_t* tokens, uint8_t* mask, int32_t* n_decoded,
+                                    int32_t* decoded_pos, double* conf, int32_t* done_seqs, int32_t* n_done,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (isnan(threshold)) return fail(FDLLM_ERR_INVALID_ARG, "threshold is NaN");
+  return run_unmask(seq, vocab, logits_dtype, logits, seq_stride, row_stride, threshold, 0, flags, tokens, mask,
+                    n_decoded, decoded_pos, conf, done_seqs, n_done, workspace, workspace_bytes, stream);
+}
+
+fdllm_status fdllm_unmask_topk(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype, const void* logits,
+                               int64_t seq_stride, int64_t row_stride, int32_t k, uint32_t flags, int32_t* tokens,
+                               uint8_t* mask, int32_t* n_decoded, int32_t* decoded_pos, double* conf,
+                               int32_t* done_seqs, int32_t* n_done, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (k < 1) return fail(FDLLM_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  return run_unmask(seq, vocab, logits_dtype, logits, seq_stride, row_stride, 0.f, k, flags, tokens, mask,
+                    n_decoded, decoded_pos, conf, done_seqs, n_done, workspace, workspace_bytes, stream);
 }
 
 fdllm_status fdllm_kv_refresh(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode,

@@ -74,6 +74,7 @@ struct UnmaskArgs {
   const void* logits;
   int vec;                  // 1: 16-byte vector loads (aligned rows)
   float tau;
+  int topk;                 // > 0: fixed-step rule (the topk most confident masked rows); 0: threshold rule
   uint32_t flags;
   int32_t* tokens;
   uint8_t* mask;

@@ -240,7 +240,18 @@ __device__ void unmask_finalize_wave(const UnmaskArgs& a, int i, int start) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) best_of(bc, bt, __shfl_xor(bc, o, 64), __shfl_xor(bt, o, 64));
   const bool fallback = bal_p == 0 && n_masked > 0;
-  const uint64_t bal_s = fallback ? (bt < 64 ? (1ull << bt) : 0ull) : bal_p;
+  uint64_t bal_s = fallback ? (bt < 64 ? (1ull << bt) : 0ull) : bal_p;
+  if (a.topk > 0) {
+    // fixed-step rule: the masked rows ranked by confidence (the lower
+    // offset first among equal ones); row t is selected when fewer than k
+    // masked rows outrank it
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+      const double cj = __shfl(conf, j, 64);
+      rank += (((bal_m >> j) & 1ull) && (cj > conf || (cj == conf && j < t))) ? 1 : 0;
+    }
+    bal_s = __ballot(mk && rank < a.topk);
+  }
   const int n_sel = __popcll(bal_s);
   const int done = (n_masked == n_sel) ? 1 : 0;
   const bool want_list = a.done_seqs || a.n_done;
@@ -288,6 +299,7 @@ __device__ void unmask_finalize_wave(const UnmaskArgs& a, int i, int start) {
 }
 
 __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
+  __shared__ double s_conf[kMaxBlockSize];  // fixed-step rule: conf of masked rows, -1 otherwise
   __shared__ int s_cnt[kUWaves][2];
   __shared__ double s_bc[kUWaves];
   __shared__ int s_bt[kUWaves];
@@ -342,6 +354,7 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
       conf[p] = mk ? 1.0 / Z : 0.0;
       tok[p] = tk;
       if (mk) best_of(bc, bt, conf[p], t);
+      if (a.topk > 0) s_conf[t] = mk ? conf[p] : -1.0;
     }
     n_masked += msk[p];
     n_pass += msk[p] && conf[p] > tau;
@@ -377,7 +390,19 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
   for (int p = 0; p < kP; ++p) {
     if (p >= np) break;
     const int t = p * kUT + tid;
-    const bool sel = msk[p] && (fallback ? (t == bt) : (conf[p] > tau));
+    bool sel = msk[p] && (fallback ? (t == bt) : (conf[p] > tau));
+    if (a.topk > 0) {
+      // fixed-step rule: fewer than k masked rows outrank row t (unmasked
+      // rows hold -1 and never do); s_conf is complete after the barrier
+      // that follows pass 1
+      int rank = 0;
+      if (msk[p])
+        for (int j = 0; j < B; ++j) {
+          const double cj = s_conf[j];
+          rank += (cj > conf[p] || (cj == conf[p] && j < t)) ? 1 : 0;
+        }
+      sel = msk[p] && rank < a.topk;
+    }
     const uint64_t bal = __ballot(sel);
     const int below = __popcll(bal & ((1ull << lane) - 1ull));
     __syncthreads();

@@ -65,6 +65,9 @@ _SIGS = [
     ("fdllm_unmask_threshold", ctypes.c_int32,
      [ctypes.POINTER(SeqDesc), ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64,
       ctypes.c_float, ctypes.c_uint32, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("fdllm_unmask_topk", ctypes.c_int32,
+     [ctypes.POINTER(SeqDesc), ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64,
+      ctypes.c_int32, ctypes.c_uint32, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     ("fdllm_kv_refresh", ctypes.c_int32,
      [ctypes.POINTER(SeqDesc), ctypes.POINTER(AttnDesc), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
     ("fdllm_workspace_init", ctypes.c_int32, [_P, ctypes.c_size_t, _P]),
@@ -194,6 +197,18 @@ def unmask_threshold(seq: SeqDesc, logits, threshold: float, tokens, mask, n_dec
                                         _ptr(tokens), _ptr(mask), _ptr(n_decoded), _ptr(decoded_pos),
                                         _ptr(conf), _ptr(done_seqs), _ptr(n_done), _ptr(workspace), nbytes,
                                         _stream(stream)))
+
+
+def unmask_topk(seq: SeqDesc, logits, k: int, tokens, mask, n_decoded, decoded_pos=None, conf=None,
+                done_seqs=None, n_done=None, workspace=None, flags: int = 0, stream=None):
+    """fdllm_unmask_topk; logits [b][B][V] (any strides, last dim contiguous)."""
+    assert logits.stride(2) == 1
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fdllm_unmask_topk(ctypes.byref(seq), logits.shape[2], _dtype_code(logits), _ptr(logits),
+                                   logits.stride(0), logits.stride(1), int(k), flags,
+                                   _ptr(tokens), _ptr(mask), _ptr(n_decoded), _ptr(decoded_pos),
+                                   _ptr(conf), _ptr(done_seqs), _ptr(n_done), _ptr(workspace), nbytes,
+                                   _stream(stream)))
 
 
 def kv_refresh(seq: SeqDesc, mode: str, k_src, v_src, k_cache, v_cache, seq_ids=None, n_seq=None,

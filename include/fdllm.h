@@ -163,6 +163,25 @@ fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, in
                                     int32_t* done_seqs, int32_t* n_done,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* One step of fixed-step decoding ([README] "Usage": a fixed number of
+ * sampling steps, so a fixed number of tokens per step -- the decoding the
+ * evaluation table's "LLaDA" and "+cache" columns use).  Same vocabulary
+ * pass, confidence and token as fdllm_unmask_threshold; the selected set is
+ * the min(k, m_i) masked rows of the current block with the largest conf_t,
+ * the lower t first among equal conf_t (compared in float64).  Outputs,
+ * flags, strides, workspace (fdllm_unmask_workspace) and alignment as in
+ * fdllm_unmask_threshold; done_seqs / n_done list the sequences whose block
+ * has no masked row left.  k >= 1, else FDLLM_ERR_INVALID_ARG; for a
+ * schedule of `steps` steps over gen_len tokens in blocks of B, k =
+ * B / (steps / (gen_len / B)). */
+fdllm_status fdllm_unmask_topk(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype,
+                               const void* logits, int64_t seq_stride, int64_t row_stride,
+                               int32_t k, uint32_t flags,
+                               int32_t* tokens, uint8_t* mask, int32_t* n_decoded,
+                               int32_t* decoded_pos, double* conf,
+                               int32_t* done_seqs, int32_t* n_done,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ */
 /* (c) KV-cache refresh at a block boundary                           */
 /* ------------------------------------------------------------------ */

@@ -114,8 +114,9 @@ def oracle_attn_subset(inp, seqs):
 # ---------------------------------------------------------------------------
 
 def run_unmask(shape, logits_np, tokens, mask, tau, ragged=False, flags=0, logits_dev=None, reps=1,
-               dtype=None):
-    """Run fdllm_unmask_threshold; returns dict of numpy outputs (of the first rep)."""
+               dtype=None, topk=None):
+    """Run fdllm_unmask_threshold (or fdllm_unmask_topk with k = topk);
+    returns dict of numpy outputs (of the first rep)."""
     s = shape
     dt = dtype or s.dtype
     keep = []
@@ -134,7 +135,10 @@ def run_unmask(shape, logits_np, tokens, mask, tau, ragged=False, flags=0, logit
         cf = torch.full((s.batch, s.block_size), -7.0, dtype=torch.float64, device=DEV)
         ds = torch.full((s.batch,), -7, dtype=torch.int32, device=DEV)
         nn = torch.full((1,), -7, dtype=torch.int32, device=DEV)
-        fd.unmask_threshold(seq, lg, tau, tk, mk, nd, dp, cf, ds, nn, ws, flags=flags)
+        if topk is None:
+            fd.unmask_threshold(seq, lg, tau, tk, mk, nd, dp, cf, ds, nn, ws, flags=flags)
+        else:
+            fd.unmask_topk(seq, lg, topk, tk, mk, nd, dp, cf, ds, nn, ws, flags=flags)
         torch.cuda.synchronize()
         r = dict(tokens=tk.cpu().numpy(), mask=mk.cpu().numpy(), n_decoded=nd.cpu().numpy(),
                  decoded_pos=dp.cpu().numpy(), conf=cf.cpu().numpy(), n_done=int(nn.item()),
