@@ -75,6 +75,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--rule", default="threshold", choices=("threshold", "topk"),
+                    help="unmask rule: confidence threshold (default) or fixed-step top-k")
+    ap.add_argument("--k", type=int, default=1, help="tokens per step of the fixed-step rule")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB between two device buffers 3 times (counter calibration) and exit")
     args = ap.parse_args()
@@ -102,6 +105,7 @@ class Bench:
         fd.lib()
         dev = "cuda"
         self.args = args
+        self.unmask_name = "unmask_topk" if args.rule == "topk" else "unmask_threshold"
         w = WORKLOADS[args.workload]
         self.w = w
         self.blocks = w["blocks"]
@@ -169,7 +173,7 @@ class Bench:
             kv_read = kv if self.mode == "dual" else 2 * b * Hkv * (L_full - nq) * d * 2 + 2 * b * Hkv * nq * d * 2
             q_out = 2 * b * nq * Hq * d * 2
             self.bytes.append({"block_attn": kv_read + q_out,
-                               "unmask_threshold": b * B * V * 2,
+                               self.unmask_name: b * B * V * 2,
                                "kv_refresh": 2 * kv if self.mode == "dual" else 0})
             self.flops.append(4 * b * Hq * nq * L_full * d)
 
@@ -193,9 +197,14 @@ class Bench:
                                                             self.vc[lr])))
         ops.append(("block_attn", lambda: fd.block_attn(seq, self.mode, q, kn, vn, self.kc[la], self.vc[la],
                                                         self.out[n], self.ws_attn[n])))
-        ops.append(("unmask_threshold", lambda: fd.unmask_threshold(
-            seq, lg, taus[call % len(taus)], self.tok[call], self.mask[call], self.n_dec, self.dpos, None,
-            self.done, self.n_done, self.ws_unmask)))
+        if self.args.rule == "topk":
+            ops.append(("unmask_topk", lambda: fd.unmask_topk(
+                seq, lg, self.args.k, self.tok[call], self.mask[call], self.n_dec, self.dpos, None,
+                self.done, self.n_done, self.ws_unmask)))
+        else:
+            ops.append(("unmask_threshold", lambda: fd.unmask_threshold(
+                seq, lg, taus[call % len(taus)], self.tok[call], self.mask[call], self.n_dec, self.dpos, None,
+                self.done, self.n_done, self.ws_unmask)))
         return ops
 
     def run_steps(self, first_step, n_steps, events=None):
@@ -399,7 +408,7 @@ def main():
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
     dk = kernels[dom]
     block_steps = K * b.nb
-    t_au = (kernels["block_attn"]["avg_us"] + kernels["unmask_threshold"]["avg_us"]) * 1e-6
+    t_au = (kernels["block_attn"]["avg_us"] + kernels[b.unmask_name]["avg_us"]) * 1e-6
     result = {
         "metric": METRIC,
         "value": round(block_steps / elapsed, 1),
@@ -414,6 +423,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": b.w["desc"], "name": args.workload, "block_steps_per_step": b.nb,
+                   "unmask_rule": args.rule if args.rule == "threshold" else f"topk k={args.k}",
                    "graph": use_graph, "rotating_sets": {"layers": args.layers, "logits": args.logit_sets}},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dk["GB_per_s"], 1), "peak": 8000.0,
                      "unit": "GB/s", "frac": round(dk["GB_per_s"] / 8000.0, 4),
