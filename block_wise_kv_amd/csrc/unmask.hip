@@ -244,13 +244,43 @@ __device__ void unmask_finalize_wave(const UnmaskArgs& a, int i, int start) {
   if (a.topk > 0) {
     // fixed-step rule: the masked rows ranked by confidence (the lower
     // offset first among equal ones); row t is selected when fewer than k
-    // masked rows outrank it
-    int rank = 0;
-    for (int j = 0; j < B; ++j) {
-      const double cj = __shfl(conf, j, 64);
-      rank += (((bal_m >> j) & 1ull) && (cj > conf || (cj == conf && j < t))) ? 1 : 0;
+    // masked rows outrank it.  k = 1 is the single best row found above and
+    // k >= n_masked takes every masked row; otherwise each lane counts the
+    // rows that outrank it, reading their confidences with readlane.
+    if (a.topk == 1) {
+      bal_s = (n_masked > 0 && bt < 64) ? (1ull << bt) : 0ull;
+    } else if (a.topk >= n_masked) {
+      bal_s = bal_m;
+    } else {
+      // every lane's confidence through LDS (wave-private, in order), read
+      // back two rows per broadcast load
+      __shared__ __attribute__((aligned(16))) double s_wconf[64];
+      s_wconf[t] = conf;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // branch-free count over a fixed 32 or 64 rows (rows past B are not
+      // in bal_m), 8 rows per group of loads
+      auto count = [&](auto nrows) __attribute__((always_inline)) {
+        int r = 0;
+#pragma unroll
+        for (int j0 = 0; j0 < decltype(nrows)::value; j0 += 8) {
+          double2 c2[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) c2[q] = *(const double2*)&s_wconf[j0 + 2 * q];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int j = j0 + q;
+            const double cj = (q & 1) ? c2[q >> 1].y : c2[q >> 1].x;
+            const int above = (int)(cj > conf) | ((int)(cj == conf) & (int)(j < t));
+            r += above & (int)((bal_m >> j) & 1ull);
+          }
+        }
+        return r;
+      };
+      const int rank = B <= 32 ? count(std::integral_constant<int, 32>{}) : count(std::integral_constant<int, 64>{});
+      bal_s = __ballot(mk && rank < a.topk);
     }
-    bal_s = __ballot(mk && rank < a.topk);
   }
   const int n_sel = __popcll(bal_s);
   const int done = (n_masked == n_sel) ? 1 : 0;
@@ -394,14 +424,21 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
     if (a.topk > 0) {
       // fixed-step rule: fewer than k masked rows outrank row t (unmasked
       // rows hold -1 and never do); s_conf is complete after the barrier
-      // that follows pass 1
-      int rank = 0;
-      if (msk[p])
-        for (int j = 0; j < B; ++j) {
-          const double cj = s_conf[j];
-          rank += (cj > conf[p] || (cj == conf[p] && j < t)) ? 1 : 0;
-        }
-      sel = msk[p] && rank < a.topk;
+      // that follows pass 1.  k = 1 is the best row bt, k >= n_masked every
+      // masked row.
+      if (a.topk == 1) {
+        sel = msk[p] && t == bt;
+      } else if (a.topk >= n_masked) {
+        sel = msk[p];
+      } else {
+        int rank = 0;
+        if (msk[p])
+          for (int j = 0; j < B; ++j) {
+            const double cj = s_conf[j];
+            rank += (cj > conf[p] || (cj == conf[p] && j < t)) ? 1 : 0;
+          }
+        sel = msk[p] && rank < a.topk;
+      }
     }
     const uint64_t bal = __ballot(sel);
     const int below = __popcll(bal & ((1ull << lane) - 1ull));
