@@ -1,0 +1,138 @@
+"""HIP-graph replay of a decoding step built from every kernel variant.
+
+The split-key attention (in-kernel merge through arrival counters), the
+8-wave GQA ring with its merge kernel, the refresh, and both unmask rules
+(per-sequence arrival counters, the finished-sequence list and the block
+advance) are captured once and replayed several times, with eager work and
+synchronisations between the replays.  Every counter is reset by its last
+user, so each replay must reproduce the eager run bit for bit; the eager
+run's attention is checked against the oracle too.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_wise_kv_amd as fd
+from gpu_util import DEV, check_attn, oracle_attn_subset, require_gpu, say, seq_for, to_dev
+from workloads import make_attn_inputs, make_decode_state, make_logits, make_refresh_src, shape_custom
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+class _Step:
+    """Device state of one step over two shapes (MHA and GQA), with the
+    pristine copies to restore it before every run."""
+
+    def __init__(self):
+        # MHA, one query tile per head: split-key kernel, 5 key chunks
+        self.s1 = shape_custom("g_mha", "bf16", 2, 4, 4, 128, [300, 200], 256, 32, [2, 5], 3000, cfg_id=70)
+        # GQA groups of 7: 8-wave ring, 8 key chunks and the merge kernel
+        self.s2 = shape_custom("g_gqa", "bf16", 2, 14, 2, 128, [500, 700], 256, 32, [1, 3], 3000, cfg_id=71)
+        self.keep = []
+        self.bidx2 = torch.from_numpy(self.s2.block_idxs.astype(np.int32)).to(DEV)
+        self.seq1 = seq_for(self.s1, True, self.keep)
+        self.seq2 = seq_for(self.s2, True, self.keep, self.bidx2)
+        self.inp1 = make_attn_inputs(self.s1, "dual")
+        self.inp2 = make_attn_inputs(self.s2, "dual")
+        d = lambda x: to_dev(x, "bf16")
+        self.q1, self.kn1, self.vn1 = d(self.inp1.q), d(self.inp1.k_new), d(self.inp1.v_new)
+        self.q2, self.kn2, self.vn2 = d(self.inp2.q), d(self.inp2.k_new), d(self.inp2.v_new)
+        self.kc1_0, self.vc1_0 = d(self.inp1.k_cache), d(self.inp1.v_cache)
+        self.kc1, self.vc1 = self.kc1_0.clone(), self.vc1_0.clone()
+        self.kc2, self.vc2 = d(self.inp2.k_cache), d(self.inp2.v_cache)
+        ks, vs = make_refresh_src(self.s1, variant=1)
+        self.ks1, self.vs1 = d(ks), d(vs)
+        self.out1 = torch.zeros_like(self.q1)
+        self.out2 = torch.zeros_like(self.q2)
+        ad1 = fd.attn_desc(4, 4, 128, fd.BF16)
+        ad2 = fd.attn_desc(14, 2, 128, fd.BF16)
+        self.ws1 = fd.new_workspace(fd.block_attn_workspace(self.seq1, ad1, "dual", self.q1.shape[1]))
+        self.ws2 = fd.new_workspace(fd.block_attn_workspace(self.seq2, ad2, "dual", self.q2.shape[1]))
+        assert self.ws1 is not None and self.ws2 is not None  # both split their keys
+        # unmask: threshold rule with block advance and done list on s2, top-k on s1
+        self.lg1 = d(make_logits(self.s1, "calibrated"))
+        self.lg2 = d(make_logits(self.s2, "calibrated"))
+        t1, m1 = make_decode_state(self.s1, [32, 7])
+        t2, m2 = make_decode_state(self.s2, [1, 32])  # sequence 0 finishes its block
+        self.tk1_0, self.mk1_0 = torch.from_numpy(t1).to(DEV), torch.from_numpy(m1).to(DEV)
+        self.tk2_0, self.mk2_0 = torch.from_numpy(t2).to(DEV), torch.from_numpy(m2).to(DEV)
+        self.bidx2_0 = self.bidx2.clone()
+        self.tk1, self.mk1 = self.tk1_0.clone(), self.mk1_0.clone()
+        self.tk2, self.mk2 = self.tk2_0.clone(), self.mk2_0.clone()
+        b = 2
+        self.nd1 = torch.zeros(b, dtype=torch.int32, device=DEV)
+        self.dp1 = torch.zeros((b, 32), dtype=torch.int32, device=DEV)
+        self.nd2 = torch.zeros(b, dtype=torch.int32, device=DEV)
+        self.dp2 = torch.zeros((b, 32), dtype=torch.int32, device=DEV)
+        self.cf2 = torch.zeros((b, 32), dtype=torch.float64, device=DEV)
+        self.ds2 = torch.zeros(b, dtype=torch.int32, device=DEV)
+        self.nn2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+        self.uws1 = fd.new_workspace(fd.unmask_workspace(self.seq1, 3000, fd.BF16))
+        self.uws2 = fd.new_workspace(fd.unmask_workspace(self.seq2, 3000, fd.BF16))
+
+    def restore(self):
+        for dst, src in ((self.kc1, self.kc1_0), (self.vc1, self.vc1_0), (self.tk1, self.tk1_0),
+                         (self.mk1, self.mk1_0), (self.tk2, self.tk2_0), (self.mk2, self.mk2_0),
+                         (self.bidx2, self.bidx2_0)):
+            dst.copy_(src)
+
+    def launch(self):
+        fd.kv_refresh(self.seq1, "dual", self.ks1, self.vs1, self.kc1, self.vc1)
+        fd.block_attn(self.seq1, "dual", self.q1, self.kn1, self.vn1, self.kc1, self.vc1, self.out1, self.ws1)
+        fd.block_attn(self.seq2, "dual", self.q2, self.kn2, self.vn2, self.kc2, self.vc2, self.out2, self.ws2)
+        fd.unmask_threshold(self.seq2, self.lg2, 0.7, self.tk2, self.mk2, self.nd2, self.dp2, self.cf2,
+                            self.ds2, self.nn2, self.uws2, flags=fd.UNMASK_ADVANCE_BLOCK)
+        fd.unmask_topk(self.seq1, self.lg1, 3, self.tk1, self.mk1, self.nd1, self.dp1, None, None, None,
+                       self.uws1)
+
+    def outputs(self):
+        return [t.clone() for t in (self.kc1, self.vc1, self.out1, self.out2, self.tk1, self.mk1, self.nd1,
+                                    self.dp1, self.tk2, self.mk2, self.nd2, self.dp2, self.cf2, self.ds2,
+                                    self.nn2, self.bidx2)]
+
+
+def test_graph_replays_match_eager():
+    st = _Step()
+    st.restore()
+    st.launch()
+    torch.cuda.synchronize()
+    ref = st.outputs()
+    # the eager step itself against the oracle (attention after the refresh)
+    from workloads import AttnInputs
+    ks_t = st.ks1.transpose(1, 2).float().cpu().numpy()
+    vs_t = st.vs1.transpose(1, 2).float().cpu().numpy()
+    inp1 = AttnInputs(st.s1, "dual", st.inp1.q, st.inp1.k_new, st.inp1.v_new, ks_t, vs_t)
+    check_attn(ref[2].float().cpu().numpy().astype(np.float64), oracle_attn_subset(inp1, [0, 1]), inp1,
+               seqs=[0, 1], label="graph step mha")
+    check_attn(ref[3].float().cpu().numpy().astype(np.float64), oracle_attn_subset(st.inp2, [1]), st.inp2,
+               seqs=[1], label="graph step gqa")
+    assert int(ref[14].item()) >= 1  # a sequence finished its block and is listed
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.restore()
+        st.launch()  # warm-up on the capture stream
+        with torch.cuda.graph(g, stream=side):
+            st.launch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st.restore()
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = st.outputs()
+        for k, (a, b_) in enumerate(zip(got, ref)):
+            # bitwise (NaN marks unmasked rows in the confidence output)
+            assert torch.equal(a.view(torch.uint8), b_.view(torch.uint8)), \
+                f"replay {rep}: output {k} differs from the eager run"
+        del junk
+    say("  graph step: 3 replays equal the eager run bit for bit")
