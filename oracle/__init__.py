@@ -28,6 +28,11 @@ Parity status of each function (pins live in tests/test_oracle_*.py):
                         masks of a small block, unread rows)
 * ``tokens_per_step``   pinned (the pages' own flag settings)
 * ``decode_block_topk_ref`` pinned (ceil(m / k) steps of k tokens)
+* ``lmhead_logits_ref`` pinned (brute-force dot products with exact sums,
+                        one-hot projection closed form, exact integer
+                        products on the grid inputs)
+* ``lmhead_unmask_ref`` pinned (equals the pinned unmask rules applied to
+                        brute-force logits; the logits' argmax on planted rows)
 * model-level quality (accuracy, real staleness drift, Theorem 1):
   parity unpinned -- needs trained weights and datasets, out of scope.
 """
@@ -42,5 +47,7 @@ from .fdllm_oracle import (  # noqa: F401
     unmask_topk_ref,
     tokens_per_step,
     decode_block_topk_ref,
+    lmhead_logits_ref,
+    lmhead_unmask_ref,
     NEAR_TIE,
 )

@@ -317,6 +317,48 @@ def tokens_per_step(gen_len: int, block_size: int, steps: int) -> int:
     return block_size // (steps // n_blocks)
 
 
+
+# ---------------------------------------------------------------------------
+# (b') the step before the confidence pass: logits from the hidden states
+# ---------------------------------------------------------------------------
+
+def lmhead_logits_ref(x, w):
+    """Logits of the block rows from their final hidden states.
+
+    The pages take a position's logits as given: its confidence is their
+    largest softmax probability and its token their argmax ([README] "Key
+    techniques" item 2).  A language model produces them by projecting the
+    final hidden state onto the vocabulary; read here as
+    logits[..., v] = sum_k x[..., k] * w[v, k], with w the [V][H] projection
+    weight and no bias.
+
+    x  [..., H] hidden states; w [V][H].  Returns float64 [..., V].
+    """
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    return x @ w.T
+
+
+def lmhead_unmask_ref(x, w, tokens, mask, prompt_lens, gen_len: int, block_size: int,
+                      block_idxs, threshold: Optional[float] = None, k: Optional[int] = None,
+                      advance: bool = False) -> UnmaskResult:
+    """One unmasking step whose logits come from the hidden states.
+
+    x [b][B][H] holds the final hidden states of the current block's rows
+    (row t <-> position P + kB + t), w [V][H] the vocabulary projection.
+    The logits are lmhead_logits_ref(x, w); the step is then the threshold
+    rule (unmask_ref, `threshold`) or the fixed-step rule (unmask_topk_ref,
+    `k`) on them, exactly one of the two given.
+    """
+    if (threshold is None) == (k is None):
+        raise ValueError("give exactly one of threshold and k")
+    logits = lmhead_logits_ref(x, w)
+    if k is None:
+        return unmask_ref(logits, tokens, mask, prompt_lens, gen_len, block_size, block_idxs,
+                          threshold, advance)
+    return unmask_topk_ref(logits, tokens, mask, prompt_lens, gen_len, block_size, block_idxs,
+                           k, advance)
+
 # ---------------------------------------------------------------------------
 # (c) cache refresh at a block boundary
 # ---------------------------------------------------------------------------

@@ -370,3 +370,85 @@ def n_masked_c5(shape: Shape) -> np.ndarray:
     """Masked positions per sequence for the ragged case: U{1..32}."""
     return rng_for(shape.cfg_id, _T_NMASK).integers(1, shape.block_size, size=shape.batch,
                                                     endpoint=True)
+
+
+# --------------------------------------------------------------------------
+# LM-head inputs: final hidden states of the block rows and the vocabulary
+# projection weight
+# --------------------------------------------------------------------------
+
+_T_LMX, _T_LMW, _T_LME = 17, 18, 19
+
+# Model width of each config's model (LLaDA-8B: 4096, Dream-7B: 3584).
+HIDDEN = {1: 256, 2: 4096, 3: 3584, 4: 4096, 5: 3584}
+
+
+@dataclasses.dataclass
+class LmheadInputs:
+    shape: Shape
+    hidden: int
+    recipe: str
+    x: np.ndarray                  # float32 [b][B][H], bf16-exact
+    w_codes: Optional[np.ndarray]  # int8 [V][H] ("grid": w == w_codes exactly), else None
+    w: Optional[np.ndarray]        # float32 [V][H], bf16-exact ("normal"), else None
+    row_exp: Optional[np.ndarray]  # int [b][B]: "grid" rows are x = codes * 2^-row_exp
+
+    def weight(self, v0: int = 0, v1: Optional[int] = None) -> np.ndarray:
+        """Rows [v0, v1) of the weight as float64."""
+        src = self.w_codes if self.w_codes is not None else self.w
+        return np.asarray(src[v0:v1], np.float64)
+
+
+def _int_chunk(flat: np.ndarray, lo: int, hi: int, ids, c: int):
+    part = flat[c * _CHUNK:(c + 1) * _CHUNK]
+    part[:] = rng_for(*ids, c).integers(lo, hi, size=part.size, endpoint=True, dtype=np.int8)
+
+
+def small_ints(shape, lo: int, hi: int, *ids: int) -> np.ndarray:
+    """int8 array of integers uniform in [lo, hi], drawn in chunks of 2^22
+    (chunk c keyed by (*ids, c))."""
+    x = np.empty(shape, np.int8)
+    flat = x.reshape(-1)
+    n_chunks = (flat.size + _CHUNK - 1) // _CHUNK
+    if n_chunks <= 1:
+        for c in range(n_chunks):
+            _int_chunk(flat, lo, hi, ids, c)
+    else:
+        import concurrent.futures
+        workers = min(16, len(os.sched_getaffinity(0)), n_chunks)
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda c: _int_chunk(flat, lo, hi, ids, c), range(n_chunks)))
+    return x
+
+
+def make_lmhead_inputs(shape: Shape, hidden: Optional[int] = None, recipe: str = "grid",
+                       variant: int = 0) -> LmheadInputs:
+    """Hidden states ``x [b][B][H]`` of the current block's rows and the
+    projection weight ``w [V][H]`` (bf16 values; logits = x w^T).
+
+    * ``"grid"``: w = integers uniform in [-3, 3]; row r of x = integers
+      uniform in [-3, 3] times 2^-e_r, e_r in {e0 - 1, e0, e0 + 1} (seeded
+      per row), e0 = round(log2(sqrt(H))).  A logit then has standard
+      deviation about 8, 4 or 2 (so rows range from unsure to confident),
+      and it is an integer multiple of 2^-e_r smaller than 9 H 2^-e_r in
+      magnitude: below 2^24 units, every fp32 sum of the products, in any
+      order, is exact.
+    * ``"normal"``: x ~ N(0, 1), w ~ N(0, 3 / sqrt(H)), both rounded to
+      bf16 (logit standard deviation about 3; fp32 accumulation rounds).
+    """
+    s = shape
+    H = int(hidden if hidden is not None else HIDDEN[s.cfg_id])
+    b, B, V = s.batch, s.block_size, s.vocab
+    ids = (s.cfg_id, variant, H)
+    if recipe == "grid":
+        e0 = int(round(0.5 * np.log2(H)))
+        e = e0 + rng_for(*ids, _T_LME).integers(-1, 1, size=(b, B), endpoint=True)
+        cx = small_ints((b, B, H), -3, 3, *ids, _T_LMX).astype(np.float32)
+        x = (cx * np.exp2(-e.astype(np.float32))[:, :, None]).astype(np.float32)
+        wc = small_ints((V, H), -3, 3, *ids, _T_LMW)
+        return LmheadInputs(s, H, recipe, x, wc, None, e)
+    if recipe == "normal":
+        x = normal((b, B, H), 1.0, "bf16", *ids, _T_LMX)
+        w = normal((V, H), 3.0 / np.sqrt(H), "bf16", *ids, _T_LMW)
+        return LmheadInputs(s, H, recipe, x, None, w, None)
+    raise ValueError(recipe)
