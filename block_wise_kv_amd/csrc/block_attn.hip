@@ -123,33 +123,8 @@ __device__ __forceinline__ const T* kv_row(const AttnArgs& a, const T* fresh, co
   return (const T*)(fr ? pf : pc);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
-
 // 16-byte chunk c of K/V tile row r is stored at chunk c ^ ring_swizzle(r).
 __device__ __forceinline__ int ring_swizzle(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-// s_waitcnt on the vector-memory counter only (vmcnt <= N), plus lgkmcnt(0)
-// when `lds` is set.
-template <int N, bool LDS>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LDS ? 0 : 15) << 8));
-}
-
-// Workgroup barrier without a memory fence: the ring's hand-offs are
-// ordered by explicit counter waits (a fence here would wait for every load
-// in flight, including the rounds being prefetched).
-__device__ __forceinline__ void ring_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 

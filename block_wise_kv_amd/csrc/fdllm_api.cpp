@@ -163,6 +163,105 @@ fdllm_status setup_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t dtyp
   return FDLLM_OK;
 }
 
+struct LmheadSetup {
+  SeqArgs sa;
+  int max_P;
+  LmheadPlan plan;
+  size_t ws;
+};
+
+fdllm_status check_lmhead_dims(int32_t vocab, int32_t hidden) {
+  if (vocab < 1) return fail(FDLLM_ERR_INVALID_ARG, "vocab must be >= 1");
+  if (vocab > (1 << 28)) return fail(FDLLM_ERR_UNSUPPORTED, "vocab > 2^28");
+  if (hidden < 8 || hidden % 8 != 0)
+    return fail(FDLLM_ERR_UNSUPPORTED, "hidden must be a positive multiple of 8 (got %d)", hidden);
+  if (hidden > (1 << 20)) return fail(FDLLM_ERR_UNSUPPORTED, "hidden > 2^20");
+  return FDLLM_OK;
+}
+
+fdllm_status setup_lmhead(const fdllm_seq_desc* seq, int32_t vocab, int32_t hidden, LmheadSetup& su) {
+  fdllm_status st = check_seq(seq, su.sa, su.max_P);
+  if (st) return st;
+  st = check_lmhead_dims(vocab, hidden);
+  if (st) return st;
+  if (seq->block_size > 1024) return fail(FDLLM_ERR_UNSUPPORTED, "block_size > 1024");
+  if (seq->batch > 65535) return fail(FDLLM_ERR_UNSUPPORTED, "batch > 65535");
+  const int64_t M = (int64_t)seq->batch * seq->block_size;
+  if (M >= ((int64_t)1 << 24)) return fail(FDLLM_ERR_UNSUPPORTED, "batch * block_size >= 2^24");
+  su.plan = plan_lmhead((int)M, vocab);
+  if ((int64_t)su.plan.grid >= ((int64_t)1 << 31)) return fail(FDLLM_ERR_INVALID_ARG, "grid too large");
+  su.ws = unmask_workspace_bytes(seq->batch, seq->block_size, su.plan.n_vwg);
+  return FDLLM_OK;
+}
+
+// The threshold rule (topk == 0) and the fixed-step rule (topk > 0) on the
+// logits of the fused vocabulary projection.
+fdllm_status run_lmhead_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t hidden, const void* x,
+                               int64_t seq_stride, int64_t row_stride, const void* w_packed, float threshold,
+                               int32_t topk, uint32_t flags, int32_t* tokens, uint8_t* mask, int32_t* n_decoded,
+                               int32_t* decoded_pos, double* conf, int32_t* done_seqs, int32_t* n_done,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  LmheadSetup su;
+  fdllm_status st = setup_lmhead(seq, vocab, hidden, su);
+  if (st) return st;
+  if (!x || !w_packed || !tokens || !mask || !n_decoded)
+    return fail(FDLLM_ERR_INVALID_ARG, "x, w_packed, tokens, mask and n_decoded must be non-NULL");
+  if (flags & ~FDLLM_UNMASK_ADVANCE_BLOCK) return fail(FDLLM_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((flags & FDLLM_UNMASK_ADVANCE_BLOCK) && !seq->block_idxs)
+    return fail(FDLLM_ERR_INVALID_ARG, "FDLLM_UNMASK_ADVANCE_BLOCK needs a device block_idxs array");
+  if (!aligned16(x) || !aligned16(w_packed))
+    return fail(FDLLM_ERR_INVALID_ARG, "x and w_packed must be 16-byte aligned");
+  if (row_stride % 8 != 0 || seq_stride % 8 != 0)
+    return fail(FDLLM_ERR_INVALID_ARG, "x strides must be multiples of 8 elements (16 bytes)");
+  if (row_stride < hidden) return fail(FDLLM_ERR_INVALID_ARG, "row_stride %lld < hidden %d", (long long)row_stride, hidden);
+  if (seq->batch > 1 && seq_stride < (int64_t)(seq->block_size - 1) * row_stride + hidden)
+    return fail(FDLLM_ERR_INVALID_ARG, "seq_stride %lld overlaps the rows of the previous sequence",
+                (long long)seq_stride);
+  if (!workspace || workspace_bytes < su.ws)
+    return fail(FDLLM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", su.ws,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(FDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const LmheadPlan& p = su.plan;
+  UnmaskArgs ua{};
+  ua.sq = su.sa;
+  ua.V = vocab;
+  ua.tau = threshold;
+  ua.topk = topk;
+  ua.flags = flags;
+  ua.tokens = tokens;
+  ua.mask = mask;
+  ua.n_decoded = n_decoded;
+  ua.decoded_pos = decoded_pos;
+  ua.conf = conf;
+  ua.done_seqs = done_seqs;
+  ua.n_done = n_done;
+  ua.nchunk = p.n_vwg;  // partials per row ([row][n_vwg] here)
+  unmask_bind_workspace(ua, workspace);
+  LmheadArgs la{};
+  la.M = seq->batch * seq->block_size;
+  la.B = seq->block_size;
+  la.H = hidden;
+  la.Hp = (hidden + kLmheadHpad - 1) / kLmheadHpad * kLmheadHpad;
+  la.V = vocab;
+  la.nvt = (vocab + 31) / 32;
+  la.n_vwg = p.n_vwg;
+  la.tiles_per_wg = p.tiles_per_wg;
+  la.n_rg = p.n_rg;
+  la.n_items = p.n_items;
+  la.per_xcd = p.per_xcd;
+  la.seq_stride = seq_stride;
+  la.row_stride = row_stride;
+  la.x = (const uint16_t*)x;
+  la.wp = (const uint4*)w_packed;
+  la.part = ua.part;
+  const LaunchEvents ev = take_launch_events();
+  hipError_t e = launch_lmhead(la, p, (hipStream_t)stream, ev.start);
+  if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "lmhead launch failed: %s", hipGetErrorString(e));
+  e = launch_lmhead_finalize(ua, ua.part, p.n_vwg, (hipStream_t)stream, ev.stop);
+  if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "lmhead finalize launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 namespace fdllm {
@@ -324,6 +423,60 @@ fdllm_status fdllm_unmask_topk(const fdllm_seq_desc* seq, int32_t vocab, int32_t
   if (k < 1) return fail(FDLLM_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
   return run_unmask(seq, vocab, logits_dtype, logits, seq_stride, row_stride, 0.f, k, flags, tokens, mask,
                     n_decoded, decoded_pos, conf, done_seqs, n_done, workspace, workspace_bytes, stream);
+}
+
+size_t fdllm_lmhead_packed_bytes(int32_t vocab, int32_t hidden) {
+  if (check_lmhead_dims(vocab, hidden)) return 0;
+  return lmhead_packed_bytes(vocab, hidden);
+}
+
+fdllm_status fdllm_lmhead_pack(int32_t vocab, int32_t hidden, const void* w, void* w_packed, size_t w_packed_bytes,
+                               void* stream) {
+  fdllm_status st = check_lmhead_dims(vocab, hidden);
+  if (st) return st;
+  if (!w || !w_packed) return fail(FDLLM_ERR_INVALID_ARG, "w and w_packed must be non-NULL");
+  if (!aligned16(w) || !aligned16(w_packed)) return fail(FDLLM_ERR_INVALID_ARG, "w and w_packed must be 16-byte aligned");
+  const size_t need = lmhead_packed_bytes(vocab, hidden);
+  if (w_packed_bytes < need)
+    return fail(FDLLM_ERR_INVALID_ARG, "w_packed needs %zu bytes (got %zu)", need, w_packed_bytes);
+  if (ranges_overlap(w, (size_t)vocab * hidden * 2, w_packed, need))
+    return fail(FDLLM_ERR_INVALID_ARG, "w_packed must not alias w");
+  hipError_t e = launch_lmhead_pack(w, w_packed, vocab, hidden, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "lmhead pack launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t fdllm_lmhead_unmask_workspace(const fdllm_seq_desc* seq, int32_t vocab, int32_t hidden) {
+  LmheadSetup su;
+  if (setup_lmhead(seq, vocab, hidden, su)) return 0;
+  return su.ws;
+}
+
+fdllm_status fdllm_lmhead_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, int32_t hidden, const void* x,
+                                           int64_t seq_stride, int64_t row_stride, const void* w_packed,
+                                           float threshold, uint32_t flags, int32_t* tokens, uint8_t* mask,
+                                           int32_t* n_decoded, int32_t* decoded_pos, double* conf,
+                                           int32_t* done_seqs, int32_t* n_done, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  if (isnan(threshold)) return fail(FDLLM_ERR_INVALID_ARG, "threshold is NaN");
+  return run_lmhead_unmask(seq, vocab, hidden, x, seq_stride, row_stride, w_packed, threshold, 0, flags, tokens,
+                           mask, n_decoded, decoded_pos, conf, done_seqs, n_done, workspace, workspace_bytes, stream);
+}
+
+fdllm_status fdllm_lmhead_unmask_topk(const fdllm_seq_desc* seq, int32_t vocab, int32_t hidden, const void* x,
+                                      int64_t seq_stride, int64_t row_stride, const void* w_packed, int32_t k,
+                                      uint32_t flags, int32_t* tokens, uint8_t* mask, int32_t* n_decoded,
+                                      int32_t* decoded_pos, double* conf, int32_t* done_seqs, int32_t* n_done,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (k < 1) return fail(FDLLM_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  return run_lmhead_unmask(seq, vocab, hidden, x, seq_stride, row_stride, w_packed, 0.f, k, flags, tokens, mask,
+                           n_decoded, decoded_pos, conf, done_seqs, n_done, workspace, workspace_bytes, stream);
+}
+
+fdllm_status fdllm_set_lmhead_tuning(int32_t vt) {
+  if (vt < 0 || vt > 2) return fail(FDLLM_ERR_INVALID_ARG, "vt must be 0, 1 or 2 (got %d)", vt);
+  set_lmhead_tuning(vt);
+  return ok();
 }
 
 fdllm_status fdllm_kv_refresh(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode,

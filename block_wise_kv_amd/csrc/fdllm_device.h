@@ -28,8 +28,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// 16 bytes as the 8 bf16 values of an MFMA operand.
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
 // 2^x on the hardware exp unit (v_exp_f32).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// s_waitcnt on the vector-memory counter only (vmcnt <= N), plus lgkmcnt(0)
+// when `LDS` is set.
+template <int N, bool LDS>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LDS ? 0 : 15) << 8));
+}
+
+// Workgroup barrier without a memory fence: hand-offs through LDS are
+// ordered by explicit counter waits (a fence here would wait for every load
+// in flight, including the ones being prefetched).
+__device__ __forceinline__ void ring_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Wave64 reductions.
 __device__ __forceinline__ float wave_max(float v) {

@@ -99,6 +99,38 @@ size_t unmask_workspace_bytes(int b, int B, int nchunk);
 void unmask_bind_workspace(UnmaskArgs& a, void* workspace);
 hipError_t launch_unmask(const UnmaskArgs& a, int dtype, hipStream_t st);
 
+// ------------------------------------------------------------------ LM head
+// The vocabulary projection fused with the confidence pass (lmhead.hip) and
+// the per-sequence finalisation of its partials (unmask.hip).
+constexpr int kLmheadHpad = 512;  // packed hidden size is a multiple of this
+
+struct LmheadArgs {
+  int M;                    // rows = b * B (row r = i * B + t)
+  int B;
+  int H, Hp;                // hidden size; padded to a multiple of kLmheadHpad
+  int V, nvt;               // vocabulary; 32-row tiles
+  int n_vwg;                // vocabulary workgroups = partials per row
+  int tiles_per_wg;         // vocabulary tiles per workgroup
+  int n_rg;                 // row groups (32 * RT rows each)
+  int n_items;              // n_vwg * n_rg
+  int per_xcd;              // work items per XCD slice of the grid
+  int64_t seq_stride, row_stride;  // hidden-state strides in elements
+  const uint16_t* x;        // bf16 hidden states
+  const uint4* wp;          // packed weight
+  UnmaskPartial* part;      // [M][n_vwg]
+};
+struct LmheadPlan {
+  int rt, vt;               // row tiles per workgroup, vocabulary tiles per wave
+  int n_vwg, n_rg, tiles_per_wg, n_items, per_xcd, grid;
+};
+LmheadPlan plan_lmhead(int M, int V);
+void set_lmhead_tuning(int vt);
+size_t lmhead_packed_bytes(int V, int H);
+hipError_t launch_lmhead_pack(const void* w, void* wp, int V, int H, hipStream_t st);
+hipError_t launch_lmhead(const LmheadArgs& a, const LmheadPlan& p, hipStream_t st, hipEvent_t ev_start);
+hipError_t launch_lmhead_finalize(const UnmaskArgs& a, const UnmaskPartial* part, int n_vwg, hipStream_t st,
+                                  hipEvent_t ev_stop);
+
 // ------------------------------------------------------------------ attention
 struct AttnArgs {
   SeqArgs sq;

@@ -182,6 +182,35 @@ __device__ void block_sum_min(double z, int idx, double* s_d, int* s_i, double& 
   }
 }
 
+// Row t's merge over the vocabulary pass's chunk partials of one sequence:
+// Z = sum of exp(logit - max) over the row, tk = its lowest argmax.  Every
+// chunk partial is loaded at once (the count is a compile-time bound), and
+// the chunk holding the maximum is rescaled by exactly 1.
+struct ChunkMerge {
+  __amdgpu_buffer_rsrc_t r;  // the sequence's partials [nchunk][B]
+  int nchunk, B;
+  __device__ __forceinline__ void operator()(int t, double& Z, int& tk) const {
+    float mc[kMaxChunks];
+    int ic[kMaxChunks];
+    double zc[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      get_partial(r, (min(c, nchunk - 1) * B + t) * (int)sizeof(UnmaskPartial), mc[c], ic[c], zc[c]);
+    float M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, mc[c]);
+    Z = 0.0;
+    tk = INT_MAX;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      if (c < nchunk) {
+        Z += zc[c] * (double)exp2_fast((mc[c] - M) * kLog2e);
+        if (mc[c] == M) tk = min(tk, ic[c]);
+      }
+    }
+  }
+};
+
 // Lexicographic max of (conf, -t): the highest confidence, lowest row on a tie.
 __device__ __forceinline__ void best_of(double& c, int& t, double c2, int t2) {
   if (c2 > c || (c2 == c && t2 < t)) {
@@ -199,36 +228,21 @@ __device__ __forceinline__ void best_of(double& c, int& t, double c2, int t2) {
 // ranks from ballots, no workgroup barrier); the finished-sequence atomic is
 // issued as soon as the row count is known, so its round trip overlaps the
 // commit stores.
-__device__ void unmask_finalize_wave(const UnmaskArgs& a, int i, int start) {
+template <class RowMerge>
+__device__ void unmask_finalize_wave(const UnmaskArgs& a, int i, int start, const RowMerge& merge) {
   const int B = a.sq.B;
   const int t = threadIdx.x;  // lane of wave 0
   int32_t* trow = a.tokens + (size_t)i * a.sq.Lcap + start;
   uint8_t* mrow = a.mask + (size_t)i * a.sq.Lcap + start;
   const double tau = (double)a.tau;
-  const __amdgpu_buffer_rsrc_t rpart = make_rsrc(a.part + (size_t)i * B * a.nchunk);
   bool mk = false;
   double conf = 0.0;
   int tok = 0;
   if (t < B) {
     mk = mrow[t] != 0;
-    float mc[kMaxChunks];
-    int ic[kMaxChunks];
-    double zc[kMaxChunks];
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      get_partial(rpart, (min(c, a.nchunk - 1) * B + t) * (int)sizeof(UnmaskPartial), mc[c], ic[c], zc[c]);
-    float M = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, mc[c]);
-    double Z = 0.0;
-    int tk = INT_MAX;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      if (c < a.nchunk) {
-        Z += zc[c] * (double)exp2_fast((mc[c] - M) * kLog2e);
-        if (mc[c] == M) tk = min(tk, ic[c]);
-      }
-    }
+    double Z;
+    int tk;
+    merge(t, Z, tk);
     conf = mk ? 1.0 / Z : 0.0;
     tok = tk;
   }
@@ -328,7 +342,8 @@ __device__ void unmask_finalize_wave(const UnmaskArgs& a, int i, int start) {
   }
 }
 
-__device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
+template <class RowMerge>
+__device__ void unmask_finalize(const UnmaskArgs& a, int i, int start, const RowMerge& merge) {
   __shared__ double s_conf[kMaxBlockSize];  // fixed-step rule: conf of masked rows, -1 otherwise
   __shared__ int s_cnt[kUWaves][2];
   __shared__ double s_bc[kUWaves];
@@ -345,7 +360,6 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
   constexpr int kP = kMaxBlockSize / kUT;
 
   // pass 1: per-row confidence, counts and the most confident masked row
-  const __amdgpu_buffer_rsrc_t rpart = make_rsrc(a.part + (size_t)i * B * a.nchunk);
   double conf[kP];
   int tok[kP];
   bool msk[kP];
@@ -360,25 +374,9 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start) {
     tok[p] = 0;
     if (p < np && t < B) {
       const bool mk = mrow[t] != 0;
-      float mc[kMaxChunks];
-      int ic[kMaxChunks];
-      double zc[kMaxChunks];
-#pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c)
-        get_partial(rpart, (min(c, a.nchunk - 1) * B + t) * (int)sizeof(UnmaskPartial), mc[c], ic[c], zc[c]);
-      float M = -INFINITY;
-#pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c) M = fmaxf(M, mc[c]);
-      double Z = 0.0;
-      int tk = INT_MAX;
-#pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c) {
-        if (c < a.nchunk) {
-          // the chunk holding the maximum is rescaled by exactly 1
-          Z += zc[c] * (double)exp2_fast((mc[c] - M) * kLog2e);
-          if (mc[c] == M) tk = min(tk, ic[c]);
-        }
-      }
+      double Z;
+      int tk;
+      merge(t, Z, tk);
       // unmasked rows carry stale partials: computed, then discarded
       msk[p] = mk;
       conf[p] = mk ? 1.0 / Z : 0.0;
@@ -667,11 +665,94 @@ __global__ __launch_bounds__(kUT) void unmask_kernel(UnmaskArgs a) {
 
   // the last of the sequence's B x nchunk workgroups finalises it
   if (!block_arrive(&a.seq_cnt[i], (unsigned)(B * a.nchunk), &s_flag)) return;
+  const ChunkMerge merge{make_rsrc(a.part + (size_t)i * B * a.nchunk), a.nchunk, B};
   if (B <= 64 && a.sq.b <= kBitsSeqs) {
-    if (tid < 64) unmask_finalize_wave(a, i, start);
+    if (tid < 64) unmask_finalize_wave(a, i, start, merge);
     return;
   }
-  unmask_finalize(a, i, start);
+  unmask_finalize(a, i, start, merge);
+}
+
+// ---- finalisation of the fused vocabulary projection (lmhead.hip)
+//
+// One workgroup per sequence.  The projection kernel left one partial
+// (max, lowest argmax, sum of exp(logit - max)) per (row, vocabulary
+// workgroup) in part[row][n_vwg]; 8 threads merge a row's partials (in
+// fp64, rescaling the running sum whenever the maximum grows), the row
+// results go through LDS, and the selection, commit and done list are the
+// vocabulary pass's finalisation.
+struct LdsMerge {
+  const double* z;
+  const int* tok;
+  __device__ __forceinline__ void operator()(int t, double& Z, int& tk) const {
+    Z = z[t];
+    tk = tok[t];
+  }
+};
+
+__device__ __forceinline__ void merge_partial(float& M, double& Z, int& I, float m, double z, int idx) {
+  if (m > M) {
+    Z = (M == -INFINITY ? 0.0 : Z * (double)exp2_fast((M - m) * kLog2e)) + z;
+    M = m;
+    I = idx;
+  } else if (m == M) {
+    Z += z;
+    I = min(I, idx);
+  } else if (m != -INFINITY) {
+    Z += z * (double)exp2_fast((m - M) * kLog2e);
+  }
+}
+
+__global__ __launch_bounds__(kUT) void lmhead_finalize_kernel(UnmaskArgs a, const UnmaskPartial* part, int nv) {
+  __shared__ double s_z[kMaxBlockSize];
+  __shared__ int s_tok[kMaxBlockSize];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int B = a.sq.B;
+  const int start = seq_prompt(a.sq, i) + seq_block(a.sq, i) * B;
+  const int j = tid & 7;
+  constexpr int kU8 = 4;  // partials in flight per thread
+  for (int t0 = 0; t0 < B; t0 += kUT / 8) {
+    const int t = t0 + (tid >> 3);
+    float M = -INFINITY;
+    double Z = 0.0;
+    int I = INT_MAX;
+    if (t < B) {
+      const UnmaskPartial* p = part + ((size_t)i * B + t) * nv;
+      for (int c0 = j; c0 < nv; c0 += 8 * kU8) {
+        UnmaskPartial q[kU8];
+#pragma unroll
+        for (int u = 0; u < kU8; ++u) q[u] = p[min(c0 + 8 * u, nv - 1)];
+#pragma unroll
+        for (int u = 0; u < kU8; ++u)
+          if (c0 + 8 * u < nv) merge_partial(M, Z, I, q[u].m, q[u].z, q[u].idx);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const float m2 = __shfl_xor(M, o, 64);
+      const double z2 = __shfl_xor(Z, o, 64);
+      const int i2 = __shfl_xor(I, o, 64);
+      merge_partial(M, Z, I, m2, z2, i2);
+    }
+    if (t < B && j == 0) {
+      s_z[t] = Z;
+      s_tok[t] = I;
+    }
+  }
+  __syncthreads();
+  const LdsMerge merge{s_z, s_tok};
+  if (B <= 64 && a.sq.b <= kBitsSeqs) {
+    if (tid < 64) unmask_finalize_wave(a, i, start, merge);
+    return;
+  }
+  unmask_finalize(a, i, start, merge);
+}
+
+hipError_t launch_lmhead_finalize(const UnmaskArgs& a, const UnmaskPartial* part, int n_vwg, hipStream_t st,
+                                  hipEvent_t ev_stop) {
+  hipEvent_t none = nullptr;
+  return launch_kernel(lmhead_finalize_kernel, dim3((unsigned)a.sq.b), dim3(kUT), 0, st, none, ev_stop, a, part,
+                       n_vwg);
 }
 
 // Workgroups the vocab split aims for (the environment variable

@@ -68,6 +68,17 @@ _SIGS = [
     ("fdllm_unmask_topk", ctypes.c_int32,
      [ctypes.POINTER(SeqDesc), ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64,
       ctypes.c_int32, ctypes.c_uint32, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("fdllm_lmhead_packed_bytes", ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
+    ("fdllm_lmhead_pack", ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
+    ("fdllm_lmhead_unmask_workspace", ctypes.c_size_t,
+     [ctypes.POINTER(SeqDesc), ctypes.c_int32, ctypes.c_int32]),
+    ("fdllm_lmhead_unmask_threshold", ctypes.c_int32,
+     [ctypes.POINTER(SeqDesc), ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64, _P,
+      ctypes.c_float, ctypes.c_uint32, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("fdllm_lmhead_unmask_topk", ctypes.c_int32,
+     [ctypes.POINTER(SeqDesc), ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64, _P,
+      ctypes.c_int32, ctypes.c_uint32, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("fdllm_set_lmhead_tuning", ctypes.c_int32, [ctypes.c_int32]),
     ("fdllm_kv_refresh", ctypes.c_int32,
      [ctypes.POINTER(SeqDesc), ctypes.POINTER(AttnDesc), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
     ("fdllm_workspace_init", ctypes.c_int32, [_P, ctypes.c_size_t, _P]),
@@ -209,6 +220,58 @@ def unmask_topk(seq: SeqDesc, logits, k: int, tokens, mask, n_decoded, decoded_p
                                    _ptr(tokens), _ptr(mask), _ptr(n_decoded), _ptr(decoded_pos),
                                    _ptr(conf), _ptr(done_seqs), _ptr(n_done), _ptr(workspace), nbytes,
                                    _stream(stream)))
+
+
+def lmhead_packed_bytes(vocab: int, hidden: int) -> int:
+    return int(lib().fdllm_lmhead_packed_bytes(vocab, hidden))
+
+
+def lmhead_pack(w, w_packed=None, stream=None):
+    """fdllm_lmhead_pack: w bf16 [V][H] contiguous -> packed weight (a new
+    uint8 device tensor unless `w_packed` is given)."""
+    assert w.dim() == 2 and w.is_contiguous()
+    V, H = w.shape
+    nbytes = lmhead_packed_bytes(V, H)
+    if w_packed is None:
+        import torch
+        w_packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=w.device)
+    _check(lib().fdllm_lmhead_pack(V, H, _ptr(w), _ptr(w_packed), w_packed.numel() * w_packed.element_size(),
+                                   _stream(stream)))
+    return w_packed
+
+
+def lmhead_unmask_workspace(seq: SeqDesc, vocab: int, hidden: int) -> int:
+    return int(lib().fdllm_lmhead_unmask_workspace(ctypes.byref(seq), vocab, hidden))
+
+
+def _lmhead_call(fn, seq, x, w_packed, vocab, rule_arg, tokens, mask, n_decoded, decoded_pos, conf, done_seqs,
+                 n_done, workspace, flags, stream):
+    assert x.stride(2) == 1
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(fn(ctypes.byref(seq), vocab, x.shape[2], _ptr(x), x.stride(0), x.stride(1), _ptr(w_packed), rule_arg,
+              flags, _ptr(tokens), _ptr(mask), _ptr(n_decoded), _ptr(decoded_pos), _ptr(conf), _ptr(done_seqs),
+              _ptr(n_done), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def lmhead_unmask_threshold(seq: SeqDesc, x, w_packed, vocab: int, threshold: float, tokens, mask, n_decoded,
+                            decoded_pos=None, conf=None, done_seqs=None, n_done=None, workspace=None,
+                            flags: int = 0, stream=None):
+    """fdllm_lmhead_unmask_threshold; x bf16 [b][B][H] (last dim contiguous)."""
+    _lmhead_call(lib().fdllm_lmhead_unmask_threshold, seq, x, w_packed, vocab, float(threshold), tokens, mask,
+                 n_decoded, decoded_pos, conf, done_seqs, n_done, workspace, flags, stream)
+
+
+def lmhead_unmask_topk(seq: SeqDesc, x, w_packed, vocab: int, k: int, tokens, mask, n_decoded,
+                       decoded_pos=None, conf=None, done_seqs=None, n_done=None, workspace=None,
+                       flags: int = 0, stream=None):
+    """fdllm_lmhead_unmask_topk; x bf16 [b][B][H] (last dim contiguous)."""
+    _lmhead_call(lib().fdllm_lmhead_unmask_topk, seq, x, w_packed, vocab, int(k), tokens, mask,
+                 n_decoded, decoded_pos, conf, done_seqs, n_done, workspace, flags, stream)
+
+
+def set_lmhead_tuning(vt: int = 0):
+    """fdllm_set_lmhead_tuning: vocabulary tiles per wave (0 = automatic)."""
+    _check(lib().fdllm_set_lmhead_tuning(int(vt)))
 
 
 def kv_refresh(seq: SeqDesc, mode: str, k_src, v_src, k_cache, v_cache, seq_ids=None, n_seq=None,

@@ -183,6 +183,69 @@ fdllm_status fdllm_unmask_topk(const fdllm_seq_desc* seq, int32_t vocab, int32_t
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ */
+/* (b') the vocabulary projection fused with the confidence pass      */
+/* ------------------------------------------------------------------ */
+
+/* The logits whose softmax maximum is the confidence and whose argmax is
+ * the token ([README] "Key techniques" item 2) come from projecting each
+ * block row's final hidden state onto the vocabulary:
+ *   logits[i][t][v] = sum_k x[i][t][k] * w[v][k]   (no bias),
+ * computed in fp32 from bf16 x and w on the matrix cores and reduced in
+ * registers; the logits are never written to memory.  The steps below then
+ * equal fdllm_unmask_threshold / fdllm_unmask_topk applied to those fp32
+ * logits (conf_t = 1 / sum_v exp(logit_v - max), tok_t = lowest argmax).
+ *
+ * w is first rearranged once into the kernel's layout: 1 KB fragments, one
+ * per (32 vocabulary rows, 16 hidden dims), each holding what a wave feeds
+ * one 32x32x16 matrix instruction; the hidden dimension is zero-padded to a
+ * multiple of 512 and the vocabulary to a multiple of 32.
+ *
+ * Sizes: 1 <= vocab <= 2^28; hidden a positive multiple of 8, <= 2^20. */
+
+/* Bytes of the packed weight for (vocab, hidden); 0 on invalid sizes. */
+size_t fdllm_lmhead_packed_bytes(int32_t vocab, int32_t hidden);
+
+/* Pack w (bf16 [vocab][hidden], row-major, contiguous) into w_packed
+ * (w_packed_bytes >= fdllm_lmhead_packed_bytes).  Both 16-byte aligned, not
+ * overlapping.  One kernel on `stream`; bit-exact rearrangement. */
+fdllm_status fdllm_lmhead_pack(int32_t vocab, int32_t hidden, const void* w, void* w_packed,
+                               size_t w_packed_bytes, void* stream);
+
+/* Workspace bytes of fdllm_lmhead_unmask_threshold / _topk (0 on invalid
+ * input).  Zero it once with fdllm_workspace_init; its counters reset
+ * themselves. */
+size_t fdllm_lmhead_unmask_workspace(const fdllm_seq_desc* seq, int32_t vocab, int32_t hidden);
+
+/* One threshold-rule step (as fdllm_unmask_threshold) on the logits of
+ * the hidden states x:
+ *   x        bf16 [b][B][hidden] addressed as x + i*seq_stride + t*row_stride
+ *            (strides in elements, multiples of 8; row_stride >= hidden;
+ *            16-byte aligned).  Every row of the block is projected; rows of
+ *            unmasked positions are computed and discarded.
+ *   w_packed the output of fdllm_lmhead_pack for the same vocab and hidden.
+ * threshold, flags, tokens, mask, n_decoded, decoded_pos, conf, done_seqs,
+ * n_done: as in fdllm_unmask_threshold.  Two kernels on `stream` (the
+ * projection, then a per-sequence finalisation); a timing-event pair armed
+ * with fdllm_set_timing_events brackets both. */
+fdllm_status fdllm_lmhead_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, int32_t hidden,
+                                           const void* x, int64_t seq_stride, int64_t row_stride,
+                                           const void* w_packed, float threshold, uint32_t flags,
+                                           int32_t* tokens, uint8_t* mask, int32_t* n_decoded,
+                                           int32_t* decoded_pos, double* conf,
+                                           int32_t* done_seqs, int32_t* n_done,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* One fixed-step step (as fdllm_unmask_topk, k >= 1) on the logits of the
+ * hidden states x; arguments as in fdllm_lmhead_unmask_threshold. */
+fdllm_status fdllm_lmhead_unmask_topk(const fdllm_seq_desc* seq, int32_t vocab, int32_t hidden,
+                                      const void* x, int64_t seq_stride, int64_t row_stride,
+                                      const void* w_packed, int32_t k, uint32_t flags,
+                                      int32_t* tokens, uint8_t* mask, int32_t* n_decoded,
+                                      int32_t* decoded_pos, double* conf,
+                                      int32_t* done_seqs, int32_t* n_done,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ */
 /* (c) KV-cache refresh at a block boundary                           */
 /* ------------------------------------------------------------------ */
 
@@ -224,8 +287,8 @@ fdllm_status fdllm_set_timing_events(void* start_event, void* stop_event);
  * FDLLM_UNMASK_TARGET_WGS also override).
  *   attn_qt     1: split-key attention kernel (one query tile per
  *               workgroup, bf16); 2 or 4: LDS-ring kernel with that many
- *               query tiles of one KV head per workgroup; 8: LDS ring with
- *               two query tiles per wave (8 per workgroup), key-chunk
+ *               query tiles of one KV head per workgroup; 8: 8-wave LDS ring
+ *               with one query tile per wave (8 per workgroup), key-chunk
  *               partials merged by a second kernel in the same call.
  *   attn_wgs    workgroups the attention key split aims for (>= 0).
  *   unmask_wgs  workgroups the unmask vocab split aims for (>= 0).
@@ -234,6 +297,13 @@ fdllm_status fdllm_set_timing_events(void* start_event, void* stop_event);
  * concurrent launches from other threads.  FDLLM_ERR_INVALID_ARG for an
  * attn_qt outside {0, 1, 2, 4, 8} or a negative target. */
 fdllm_status fdllm_set_tuning(int32_t attn_qt, int32_t attn_wgs, int32_t unmask_wgs);
+
+/* Planner override of the fused vocabulary projection: vocabulary tiles of
+ * 32 rows per wave (1 or 2; 0 = automatic, which the environment variable
+ * FDLLM_LMHEAD_VT also overrides).  Blocks of more than 64 rows per batch
+ * always use 1.  Process-wide; query fdllm_lmhead_unmask_workspace again
+ * afterwards.  FDLLM_ERR_INVALID_ARG outside {0, 1, 2}. */
+fdllm_status fdllm_set_lmhead_tuning(int32_t vt);
 
 const char* fdllm_status_string(int32_t status);
 const char* fdllm_last_error(void);

@@ -187,3 +187,38 @@ def compare_unmask(g, ref, shape, label="", tau=None):
     say(f"  {label}: decisions bit-exact; near-tie rows excluded = {excluded}; top-2 ties compared = {top2}; "
         f"tokens decoded = {int(ref.n_decoded.sum())}")
     return excluded
+
+
+def lmhead_weight_dev(inp):
+    """The projection weight of a workloads.LmheadInputs as a bf16 device tensor."""
+    if inp.w_codes is not None:
+        return torch.from_numpy(inp.w_codes).to(DEV).to(torch.bfloat16)  # small integers: exact
+    return to_dev(inp.w, "bf16")
+
+
+def run_lmhead(shape, inp, tokens, mask, tau=None, topk=None, ragged=False, flags=0, x_dev=None, w_packed=None):
+    """Run fdllm_lmhead_unmask_threshold (or _topk with k = topk) on the hidden
+    states of `inp`; returns a dict of numpy outputs like run_unmask."""
+    s = shape
+    keep = []
+    bidx = torch.from_numpy(s.block_idxs.astype(np.int32)).to(DEV) if (ragged or flags) else None
+    seq = seq_for(s, ragged or bool(flags), keep, bidx)
+    x = x_dev if x_dev is not None else to_dev(inp.x, "bf16")
+    wp = w_packed if w_packed is not None else fd.lmhead_pack(lmhead_weight_dev(inp))
+    ws = fd.new_workspace(fd.lmhead_unmask_workspace(seq, s.vocab, inp.hidden))
+    tk = torch.from_numpy(tokens.astype(np.int32)).to(DEV)
+    mk = torch.from_numpy(mask.astype(np.uint8)).to(DEV)
+    nd = torch.full((s.batch,), -7, dtype=torch.int32, device=DEV)
+    dp = torch.full((s.batch, s.block_size), -7, dtype=torch.int32, device=DEV)
+    cf = torch.full((s.batch, s.block_size), -7.0, dtype=torch.float64, device=DEV)
+    ds = torch.full((s.batch,), -7, dtype=torch.int32, device=DEV)
+    nn = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    if topk is None:
+        fd.lmhead_unmask_threshold(seq, x, wp, s.vocab, tau, tk, mk, nd, dp, cf, ds, nn, ws, flags=flags)
+    else:
+        fd.lmhead_unmask_topk(seq, x, wp, s.vocab, topk, tk, mk, nd, dp, cf, ds, nn, ws, flags=flags)
+    torch.cuda.synchronize()
+    return dict(tokens=tk.cpu().numpy(), mask=mk.cpu().numpy(), n_decoded=nd.cpu().numpy(),
+                decoded_pos=dp.cpu().numpy(), conf=cf.cpu().numpy(), n_done=int(nn.item()),
+                done_seqs=ds.cpu().numpy()[:max(0, int(nn.item()))],
+                block_idxs=bidx.cpu().numpy() if bidx is not None else None)

@@ -177,3 +177,70 @@ def test_set_tuning_rejects_and_replans():
     assert one == 0 and many > 0  # one key chunk needs no partials
     # 8 key chunks of fp32 partials (O, m, l per row) for 8 x 28 heads x 32 rows
     assert one8 == 0 and auto8 == 8 * 28 * 8 * (32 * 128 + 64) * 4
+
+
+def _lm_call(seq, vocab=126464, hidden=4096, x=P1, ss=None, rs=None, wp=P2, tau=0.9, k=None, flags=0, ws=P7,
+             wsb=1 << 30):
+    L = fd.lib()
+    rs = hidden if rs is None else rs
+    ss = seq.block_size * rs if ss is None else ss
+    if k is None:
+        st = L.fdllm_lmhead_unmask_threshold(ctypes.byref(seq), vocab, hidden, x, ss, rs, wp, tau, flags, P3, P4,
+                                             P5, P6, None, None, None, ws, wsb, None)
+    else:
+        st = L.fdllm_lmhead_unmask_topk(ctypes.byref(seq), vocab, hidden, x, ss, rs, wp, k, flags, P3, P4, P5, P6,
+                                        None, None, None, ws, wsb, None)
+    return st, L.fdllm_last_error().decode()
+
+
+@pytest.mark.parametrize("case, seq, kw, status, msg", [
+    ("nan tau", _seq(), {"tau": float("nan")}, 1, "NaN"),
+    ("k zero", _seq(), {"k": 0}, 1, "k must be"),
+    ("vocab", _seq(), {"vocab": 0}, 1, "vocab"),
+    ("hidden odd", _seq(), {"hidden": 4092}, 2, "multiple of 8"),
+    ("hidden small", _seq(), {"hidden": 0}, 2, "multiple of 8"),
+    ("flags", _seq(), {"flags": 2}, 1, "flags"),
+    ("advance", _seq(), {"flags": 1}, 1, "block_idxs"),
+    ("x align", _seq(), {"x": P1 + 8}, 1, "aligned"),
+    ("w align", _seq(), {"wp": P2 + 4}, 1, "aligned"),
+    ("stride align", _seq(), {"rs": 4100}, 1, "multiples of 8"),
+    ("row stride", _seq(), {"rs": 4088, "hidden": 4096}, 1, "row_stride"),
+    ("seq stride", _seq(batch=2), {"ss": 4096}, 1, "seq_stride"),
+    ("no x", _seq(), {"x": None}, 1, "non-NULL"),
+    ("no ws", _seq(), {"ws": None, "wsb": 0}, 3, "workspace"),
+    ("small ws", _seq(), {"wsb": 64}, 3, "workspace"),
+    ("big block", _seq(gen_len=2048, block_size=2048, max_seq_len=4096), {}, 2, "block_size"),
+])
+def test_lmhead_rejects(case, seq, kw, status, msg):
+    st, err = _lm_call(seq, **kw)
+    assert st == status, (case, st, err)
+    assert msg in err
+
+
+def test_lmhead_sizes_and_pack_rejects():
+    L = fd.lib()
+    # vocabulary padded to 32 rows, hidden size to a multiple of 512
+    assert fd.lmhead_packed_bytes(126464, 4096) == 126464 * 4096 * 2
+    assert fd.lmhead_packed_bytes(152064, 3584) == 152064 * 3584 * 2  # 3584 = 7 x 512
+    assert fd.lmhead_packed_bytes(3000, 200) == 3008 * 512 * 2
+    assert fd.lmhead_packed_bytes(0, 4096) == 0 and fd.lmhead_packed_bytes(10, 12) == 0
+    need = fd.lmhead_packed_bytes(1000, 512)
+    assert L.fdllm_lmhead_pack(1000, 512, P1, P2, need - 16, None) == 1
+    assert "bytes" in L.fdllm_last_error().decode()
+    assert L.fdllm_lmhead_pack(1000, 512, P1, P1 + 4096, need, None) == 1
+    assert "alias" in L.fdllm_last_error().decode()
+    assert L.fdllm_lmhead_pack(1000, 512, None, P2, need, None) == 1
+    assert L.fdllm_lmhead_pack(1000, 516, P1, P2, need, None) == 2
+    # workspace: 16-byte partials per (row, vocabulary workgroup) + counters
+    n = fd.lmhead_unmask_workspace(_seq(), 126464, 4096)
+    assert n > 32 * 16 * 240 and n % 256 == 0
+    assert fd.lmhead_unmask_workspace(_seq(), 126464, 4090) == 0
+    with pytest.raises(fd.FdllmError):
+        fd.set_lmhead_tuning(3)
+    try:
+        fd.set_lmhead_tuning(1)
+        n1 = fd.lmhead_unmask_workspace(_seq(), 126464, 4096)
+    finally:
+        fd.set_lmhead_tuning(0)
+    # one vocabulary tile per wave doubles the workgroups (and partials)
+    assert n1 > 1.9 * n
