@@ -26,6 +26,14 @@ runs on.
 DualCache and prefix cache, large-batch LLaDA-8B); the default is the one
 above.  Prints one JSON line.  --gpus N > 1 is refused: this path runs on one
 GPU.
+
+--lmhead measures the step before the unmask instead: the vocabulary
+projection fused with the confidence pass (fdllm_lmhead_unmask_threshold,
+the logits never written) on the workload's rows (c2: 32 rows, hidden 4096,
+vocabulary 126464; c3: 256 rows, hidden 3584, vocabulary 152064; c4: 1024
+rows, hidden 4096), K calls replayed from a HIP graph, then per-call events;
+beside it the unfused path (torch's linear layer writing bf16 logits, then
+fdllm_unmask_threshold reading them) for comparison.
 """
 import argparse
 import json
@@ -78,12 +86,14 @@ def parse():
     ap.add_argument("--rule", default="threshold", choices=("threshold", "topk"),
                     help="unmask rule: confidence threshold (default) or fixed-step top-k")
     ap.add_argument("--k", type=int, default=1, help="tokens per step of the fixed-step rule")
+    ap.add_argument("--lmhead", action="store_true",
+                    help="measure the fused vocabulary projection + unmask (c2, c3 or c4 rows)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB between two device buffers 3 times (counter calibration) and exit")
     args = ap.parse_args()
     w = WORKLOADS[args.workload]
     for key in ("steps", "warmup", "layers", "logit_sets"):
-        if getattr(args, key) is None:
+        if getattr(args, key) is None and not (args.lmhead and key in ("steps", "warmup")):
             setattr(args, key, w[key])
     return args
 
@@ -337,6 +347,172 @@ def copy_probe(mib: int):
     print(json.dumps({"copy_probe_bytes": n * 4, "copies": 3}), flush=True)
 
 
+# LM-head workloads: the rows of one decoding step of the same configs.
+LMHEAD = {
+    "c2": dict(desc="LLaDA-8B LM head fused with the threshold unmask: batch 1 x block 32 = 32 rows, hidden 4096, "
+                    "vocab 126464, tau 0.9", shape="c2", hidden=4096, steps=50, warmup=5),
+    "c3": dict(desc="Dream-7B LM head fused with the threshold unmask: batch 8 x block 32 = 256 rows, hidden 3584, "
+                    "vocab 152064, tau 0.9", shape="c3", hidden=3584, steps=20, warmup=3),
+    "c4": dict(desc="LLaDA-8B LM head fused with the threshold unmask: batch 32 x block 32 = 1024 rows, hidden 4096, "
+                    "vocab 126464, tau 0.9", shape="c4", hidden=4096, steps=8, warmup=2),
+}
+PEAK_BF16_FLOPS = 2.5e15
+
+
+def lmhead_cpu_baseline(inp, s, tokens, mask, tau, seconds):
+    """The fp64 oracle's LM-head step (projection + threshold unmask) on the
+    host, one thread, whole calls until the time budget is spent."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import lmhead_unmask_ref
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            lmhead_unmask_ref(inp.x, inp.weight(), tokens, mask, s.prompt_lens, s.gen_len, s.block_size,
+                              s.block_idxs, threshold=tau)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": done / el, "unit": "calls/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} whole LM-head + unmask calls of this workload in {el:.1f} s (fp64 NumPy oracle, "
+                      "weight converted to fp64 inside each call, BLAS limited to 1 thread)"}
+
+
+def lmhead_main(args):
+    import numpy as np
+    import torch
+
+    import block_wise_kv_amd as fd
+    from workloads import make_decode_state, make_lmhead_inputs, shape_c2, shape_c3, shape_c4
+
+    if args.workload not in LMHEAD:
+        print(f"--lmhead supports workloads {sorted(LMHEAD)}", file=sys.stderr)
+        sys.exit(2)
+    cfg = LMHEAD[args.workload]
+    s = {"c2": shape_c2, "c3": shape_c3, "c4": shape_c4}[cfg["shape"]]()
+    H, V, M = cfg["hidden"], s.vocab, s.batch * s.block_size
+    K = args.steps or cfg["steps"]
+    W = args.warmup if args.warmup is not None else cfg["warmup"]
+    tau = 0.9
+    inp = make_lmhead_inputs(s, H)
+    dev = "cuda"
+    x = torch.from_numpy(inp.x).to(dev).to(torch.bfloat16)
+    w = torch.from_numpy(inp.w_codes).to(dev).to(torch.bfloat16)
+    wp = fd.lmhead_pack(w)
+    seq = fd.seq_desc(s.batch, s.max_seq_len, s.gen_len, s.block_size, int(s.prompt_lens[0]), int(s.block_idxs[0]))
+    tokens, mask = make_decode_state(s, None)
+    tk0 = torch.from_numpy(tokens).to(dev)
+    mk0 = torch.from_numpy(mask).to(dev)
+    n = W + K
+    tks = [tk0.clone() for _ in range(n)]
+    mks = [mk0.clone() for _ in range(n)]
+    nd = torch.zeros(s.batch, dtype=torch.int32, device=dev)
+    ws = fd.new_workspace(fd.lmhead_unmask_workspace(seq, V, H))
+
+    def reset():
+        for t in tks:
+            t.copy_(tk0)
+        for m in mks:
+            m.copy_(mk0)
+
+    def call(j):
+        fd.lmhead_unmask_threshold(seq, x, wp, V, tau, tks[j], mks[j], nd, workspace=ws)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        g_warm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_warm, stream=stream):
+            for j in range(W):
+                call(j)
+        g_timed = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_timed, stream=stream):
+            for j in range(W, n):
+                call(j)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    g_warm.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g_timed.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # per-call events (both kernels of a call), eager on the default stream
+    reset()
+    torch.cuda.synchronize()
+    events = HipEvents(2 * K)
+    for m, j in enumerate(range(W, n)):
+        fd.set_timing_events(events.ev[2 * m], events.ev[2 * m + 1])
+        call(j)
+    torch.cuda.synchronize()
+    t_call = sum(events.elapsed_s(2 * m, 2 * m + 1) for m in range(K)) / K
+    events.close()
+
+    # the unfused path: torch's linear layer writes bf16 logits, the unmask reads them
+    x2 = x.view(M, H)
+    logits = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+    uws = fd.new_workspace(fd.unmask_workspace(seq, V, fd.BF16))
+    reset()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_gemm = t_unm = 0.0
+    for j in range(n):
+        e[0].record()
+        torch.mm(x2, w.t(), out=logits)  # 2-D product (not batched): logits = x w^T
+        e[1].record()
+        fd.unmask_threshold(seq, logits.view(s.batch, s.block_size, V), tau, tks[j], mks[j], nd, workspace=uws)
+        e[2].record()
+        torch.cuda.synchronize()
+        if j >= W:
+            t_gemm += e[0].elapsed_time(e[1]) * 1e-3
+            t_unm += e[1].elapsed_time(e[2]) * 1e-3
+    t_gemm /= K
+    t_unm /= K
+
+    wbytes = V * H * 2
+    alg_bytes = wbytes + M * H * 2
+    flops = 2.0 * M * V * H
+    hbm = flops / alg_bytes < PEAK_BF16_FLOPS / PEAK_HBM_BPS
+    if hbm:
+        roof = {"bound": "hbm", "kernel": "lmhead_unmask", "achieved": round(alg_bytes / t_call / 1e9, 1),
+                "peak": 8000.0, "unit": "GB/s", "frac": round(alg_bytes / t_call / PEAK_HBM_BPS, 4)}
+    else:
+        roof = {"bound": "mfma", "kernel": "lmhead_unmask", "achieved": round(flops / t_call / 1e12, 1),
+                "peak": 2500.0, "unit": "TFLOP/s", "frac": round(flops / t_call / PEAK_BF16_FLOPS, 4)}
+    roof["traffic"] = measured_traffic("lm_" + args.workload, "lmhead_unmask")
+    roof["algorithmic_bytes"] = alg_bytes
+    roof["flops"] = flops
+    result = {
+        "metric": "fused LM-head projection + threshold unmask calls/s (logits never written), 1 GPU",
+        "value": round(K / elapsed, 2),
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["desc"], "name": "lm_" + args.workload, "rows": M, "hidden": H, "vocab": V,
+                   "graph": True},
+        "roofline": roof,
+        "kernels": {"lmhead_unmask": {"avg_us": round(t_call * 1e6, 3), "launches": K, "bytes": alg_bytes,
+                                      "GB_per_s": round(alg_bytes / t_call / 1e9, 1),
+                                      "TFLOP_per_s": round(flops / t_call / 1e12, 2)}},
+        "unfused": {"linear_us": round(t_gemm * 1e6, 2), "unmask_us": round(t_unm * 1e6, 2),
+                    "total_us": round((t_gemm + t_unm) * 1e6, 2),
+                    "speedup_of_fused": round((t_gemm + t_unm) / t_call, 3)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = lmhead_cpu_baseline(inp, s, tokens, mask, tau, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -346,6 +522,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decoding hot path is "
               "measured on a single MI355X and has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
+    if args.lmhead:
+        lmhead_main(args)
+        return
     import torch
 
     b = Bench(args)

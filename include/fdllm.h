@@ -300,8 +300,8 @@ fdllm_status fdllm_set_tuning(int32_t attn_qt, int32_t attn_wgs, int32_t unmask_
 
 /* Planner override of the fused vocabulary projection: vocabulary tiles of
  * 32 rows per wave (1 or 2; 0 = automatic, which the environment variable
- * FDLLM_LMHEAD_VT also overrides).  Blocks of more than 64 rows per batch
- * always use 1.  Process-wide; query fdllm_lmhead_unmask_workspace again
+ * FDLLM_LMHEAD_VT also overrides).  Calls with more than 64 rows (batch x
+ * block size) always use 1.  Process-wide; query fdllm_lmhead_unmask_workspace again
  * afterwards.  FDLLM_ERR_INVALID_ARG outside {0, 1, 2}. */
 fdllm_status fdllm_set_lmhead_tuning(int32_t vt);
 

@@ -240,7 +240,10 @@ def test_lmhead_sizes_and_pack_rejects():
     try:
         fd.set_lmhead_tuning(1)
         n1 = fd.lmhead_unmask_workspace(_seq(), 126464, 4096)
+        fd.set_lmhead_tuning(2)
+        n2 = fd.lmhead_unmask_workspace(_seq(), 126464, 4096)
     finally:
         fd.set_lmhead_tuning(0)
-    # one vocabulary tile per wave doubles the workgroups (and partials)
-    assert n1 > 1.9 * n
+    # one vocabulary tile per wave (the default for 32 rows) has twice the
+    # workgroups (and partials) of two
+    assert n1 == n and n1 > 1.9 * n2

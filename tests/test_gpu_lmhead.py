@@ -37,7 +37,9 @@ def _ref(s, inp, tokens, mask, tau=None, k=None, advance=False):
 CASES = [
     ("b1_rt1", 1, 32, 512, 3000, [64], [1], [20], 90),          # one row tile, ragged last vocabulary tile
     ("b2_rt2_h200", 2, 32, 200, 1000, [40, 70], [0, 2], [32, 9], 91),  # hidden padded 200 -> 512
-    ("b5_rt4", 5, 32, 1024, 5000, [100], [3], [17], 92),         # 160 rows: two row groups, the second partial
+    ("b3_rt4", 3, 32, 1024, 5000, [100], [3], [17], 92),         # 96 rows: 4 row tiles, the last one empty
+    ("b5_rt8", 5, 32, 512, 2300, [100], [3], [17], 89),          # 160 rows: 8 row tiles, 3 of them empty
+    ("b9_rt8x2", 9, 32, 256, 1200, [20], [0], [30], 88),         # 288 rows: two row groups of 256
     ("B64", 1, 64, 256, 2000, [30], [1], [50], 93),              # 64-row block, one-wave finalisation
     ("B128", 2, 128, 256, 700, [10, 20], [0, 1], [128, 40], 94),  # 128-row block, workgroup finalisation
 ]
