@@ -677,7 +677,7 @@ __global__ __launch_bounds__(kUT) void unmask_kernel(UnmaskArgs a) {
 //
 // One workgroup per sequence.  The projection kernel left one partial
 // (max, lowest argmax, sum of exp(logit - max)) per (row, vocabulary
-// workgroup) in part[row][n_vwg]; 8 threads merge a row's partials (in
+// workgroup) in part[row][n_vwg]; up to 32 threads merge a row's partials (in
 // fp64, rescaling the running sum whenever the maximum grows), the row
 // results go through LDS, and the selection, commit and done list are the
 // vocabulary pass's finalisation.
@@ -703,32 +703,37 @@ __device__ __forceinline__ void merge_partial(float& M, double& Z, int& I, float
   }
 }
 
-__global__ __launch_bounds__(kUT) void lmhead_finalize_kernel(UnmaskArgs a, const UnmaskPartial* part, int nv) {
+// NT threads: 1024 when the one-wave finalisation applies (blocks of up to
+// 64 rows), so that up to 32 threads share a row's partials; 256 otherwise.
+template <int NT>
+__global__ __launch_bounds__(NT) void lmhead_finalize_kernel(UnmaskArgs a, const UnmaskPartial* part, int nv) {
   __shared__ double s_z[kMaxBlockSize];
   __shared__ int s_tok[kMaxBlockSize];
   const int i = blockIdx.x, tid = threadIdx.x;
   const int B = a.sq.B;
   const int start = seq_prompt(a.sq, i) + seq_block(a.sq, i) * B;
-  const int j = tid & 7;
-  constexpr int kU8 = 4;  // partials in flight per thread
-  for (int t0 = 0; t0 < B; t0 += kUT / 8) {
-    const int t = t0 + (tid >> 3);
+  // threads per row: the largest power of two up to 32 with tpr * B <= NT
+  int tpr = 1;
+  while (tpr < 32 && 2 * tpr * B <= NT) tpr *= 2;
+  const int j = tid & (tpr - 1);
+  constexpr int kU8 = 8;  // partials in flight per thread
+  for (int t0 = 0; t0 < B; t0 += NT / tpr) {
+    const int t = t0 + tid / tpr;
     float M = -INFINITY;
     double Z = 0.0;
     int I = INT_MAX;
     if (t < B) {
       const UnmaskPartial* p = part + ((size_t)i * B + t) * nv;
-      for (int c0 = j; c0 < nv; c0 += 8 * kU8) {
+      for (int c0 = j; c0 < nv; c0 += tpr * kU8) {
         UnmaskPartial q[kU8];
 #pragma unroll
-        for (int u = 0; u < kU8; ++u) q[u] = p[min(c0 + 8 * u, nv - 1)];
+        for (int u = 0; u < kU8; ++u) q[u] = p[min(c0 + tpr * u, nv - 1)];
 #pragma unroll
         for (int u = 0; u < kU8; ++u)
-          if (c0 + 8 * u < nv) merge_partial(M, Z, I, q[u].m, q[u].z, q[u].idx);
+          if (c0 + tpr * u < nv) merge_partial(M, Z, I, q[u].m, q[u].z, q[u].idx);
       }
     }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
+    for (int o = 1; o < tpr; o <<= 1) {
       const float m2 = __shfl_xor(M, o, 64);
       const double z2 = __shfl_xor(Z, o, 64);
       const int i2 = __shfl_xor(I, o, 64);
@@ -745,13 +750,16 @@ __global__ __launch_bounds__(kUT) void lmhead_finalize_kernel(UnmaskArgs a, cons
     if (tid < 64) unmask_finalize_wave(a, i, start, merge);
     return;
   }
-  unmask_finalize(a, i, start, merge);
+  if constexpr (NT == kUT) unmask_finalize(a, i, start, merge);  // the launch picks 256 threads here
 }
 
 hipError_t launch_lmhead_finalize(const UnmaskArgs& a, const UnmaskPartial* part, int n_vwg, hipStream_t st,
                                   hipEvent_t ev_stop) {
   hipEvent_t none = nullptr;
-  return launch_kernel(lmhead_finalize_kernel, dim3((unsigned)a.sq.b), dim3(kUT), 0, st, none, ev_stop, a, part,
+  if (a.sq.B <= 64 && a.sq.b <= kBitsSeqs)
+    return launch_kernel(lmhead_finalize_kernel<1024>, dim3((unsigned)a.sq.b), dim3(1024), 0, st, none, ev_stop, a,
+                         part, n_vwg);
+  return launch_kernel(lmhead_finalize_kernel<kUT>, dim3((unsigned)a.sq.b), dim3(kUT), 0, st, none, ev_stop, a, part,
                        n_vwg);
 }
 
