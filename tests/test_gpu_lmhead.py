@@ -171,7 +171,7 @@ def test_continuous_inputs_within_rounding_bound():
     say(f"  continuous: worst conf error / bound = {worst:.3f}; E max = {E.max():.2e}")
 
 
-def _big_case(shape, H, tau=None, k=None, label=""):
+def _big_case(shape, H, tau=None, k=None, label="", seqs=None):
     inp = make_lmhead_inputs(shape, H)
     s = shape
     tokens, mask = make_decode_state(s, None)
@@ -181,16 +181,22 @@ def _big_case(shape, H, tau=None, k=None, label=""):
     g = run_lmhead(s, inp, tokens, mask, tau=tau, topk=k, w_packed=wp)
     del wp
     torch.cuda.empty_cache()
-    # oracle logits by vocabulary chunks (the same definition per chunk)
-    x = inp.x
+    # oracle logits by vocabulary chunks (the same definition per chunk), for
+    # the sampled sequences (a sequence's step depends on its own rows only)
+    sel = list(range(s.batch)) if seqs is None else list(seqs)
+    x = inp.x[sel]
     chunks = []
     step = 16384
     for v0 in range(0, s.vocab, step):
         chunks.append(lmhead_logits_ref(x, inp.weight(v0, v0 + step)))
     logits = np.concatenate(chunks, axis=-1)
-    args = (tokens, mask, s.prompt_lens, s.gen_len, s.block_size, s.block_idxs)
+    sub = shape_custom(s.name, s.dtype, len(sel), s.n_q_heads, s.n_kv_heads, s.head_dim, s.prompt_lens[sel],
+                       s.gen_len, s.block_size, s.block_idxs[sel], s.vocab, s.max_seq_len, cfg_id=s.cfg_id)
+    args = (tokens[sel], mask[sel], sub.prompt_lens, sub.gen_len, sub.block_size, sub.block_idxs)
     ref = unmask_ref(logits, *args, tau) if k is None else unmask_topk_ref(logits, *args, k)
-    compare_unmask(g, ref, s, label=label)
+    gs = {key: (v[sel] if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == s.batch else v)
+          for key, v in g.items()}
+    compare_unmask(gs, ref, sub, label=label)
 
 
 def test_llada8b_full_size():
@@ -203,3 +209,12 @@ def test_dream7b_full_size_topk():
     # Dream-7B: hidden 3584, vocabulary 152064, 8 sequences (256 rows: two row groups)
     say("lmhead full size: Dream-7B b8")
     _big_case(shape_c3(), 3584, k=2, label="lmhead dream7b b8 k2")
+
+
+def test_llada8b_b32_full_size_sampled():
+    # LLaDA-8B at batch 32 (1024 rows: four row groups of 256), the shape
+    # bench.py --lmhead --workload c4 times; sequences 0, 13 and 31 checked
+    # against the oracle (each sequence's step depends only on its own rows)
+    from workloads import shape_c4
+    say("lmhead full size: LLaDA-8B b32 (sampled sequences)")
+    _big_case(shape_c4(), 4096, tau=0.7, label="lmhead llada8b b32 tau0.7", seqs=[0, 13, 31])
