@@ -332,6 +332,27 @@ def measured_traffic(workload: str, kernel: str):
     return int(round(k["fetch_kib"] * 1024 * data["fetch_scale"] + k["write_kib"] * 1024 * data["write_scale"]))
 
 
+def large_copy_rate() -> float:
+    """Bytes/s (read + write) of a plain 1 GiB device-to-device copy, the
+    measured reference beside the 8 TB/s peak."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / 5
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * n * 4 / t
+
+
 def copy_probe(mib: int):
     """A plain device copy of known size, for scaling the HBM byte counters
     (FETCH_SIZE / WRITE_SIZE) of the profiler: each copy reads and writes
@@ -567,6 +588,7 @@ def main():
     torch.cuda.synchronize()
 
     elapsed = t1 - t0
+    copy_bps = large_copy_rate()
     per = {}
     for m, (name, n) in enumerate(names):
         t = events.elapsed_s(2 * m, 2 * m + 1)
@@ -581,7 +603,8 @@ def main():
         avg = e["t"] / e["n"]
         gbs = e["bytes"] / e["t"] / 1e9
         kernels[name] = {"avg_us": round(avg * 1e6, 3), "launches": e["n"], "bytes": e["bytes"] // e["n"],
-                         "GB_per_s": round(gbs, 1), "frac_of_8TBps": round(gbs * 1e9 / PEAK_HBM_BPS, 4)}
+                         "GB_per_s": round(gbs, 1), "frac_of_8TBps": round(gbs * 1e9 / PEAK_HBM_BPS, 4),
+                         "frac_of_copy": round(gbs * 1e9 / copy_bps, 4)}
         if name == "block_attn":
             kernels[name]["TFLOP_per_s"] = round(e["flops"] / e["t"] / 1e12, 2)
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
@@ -608,6 +631,7 @@ def main():
                      "unit": "GB/s", "frac": round(dk["GB_per_s"] / 8000.0, 4),
                      "traffic": measured_traffic(args.workload, dom), "algorithmic_bytes": dk["bytes"]},
         "kernels": kernels,
+        "large_copy_GB_per_s": round(copy_bps / 1e9, 1),
         "attn_unmask_block_steps_per_s": round(1.0 / t_au, 1),
     }
     if not args.no_cpu_baseline and args.workload == "c2":

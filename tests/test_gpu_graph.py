@@ -1,9 +1,10 @@
 """HIP-graph replay of a decoding step built from every kernel variant.
 
 The split-key attention (in-kernel merge through arrival counters), the
-8-wave GQA ring with its merge kernel, the refresh, and both unmask rules
+8-wave GQA ring with its merge kernel, the refresh, both unmask rules
 (per-sequence arrival counters, the finished-sequence list and the block
-advance) are captured once and replayed several times, with eager work and
+advance) and the fused LM head with its finalisation are captured once and
+replayed several times, with eager work and
 synchronisations between the replays.  Every counter is reset by its last
 user, so each replay must reproduce the eager run bit for bit; the eager
 run's attention is checked against the oracle too.
@@ -14,7 +15,8 @@ import torch
 
 import block_wise_kv_amd as fd
 from gpu_util import DEV, check_attn, oracle_attn_subset, require_gpu, say, seq_for, to_dev
-from workloads import make_attn_inputs, make_decode_state, make_logits, make_refresh_src, shape_custom
+from workloads import (make_attn_inputs, make_decode_state, make_lmhead_inputs, make_logits, make_refresh_src,
+                       shape_custom)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,11 +76,24 @@ class _Step:
         self.nn2 = torch.zeros(1, dtype=torch.int32, device=DEV)
         self.uws1 = fd.new_workspace(fd.unmask_workspace(self.seq1, 3000, fd.BF16))
         self.uws2 = fd.new_workspace(fd.unmask_workspace(self.seq2, 3000, fd.BF16))
+        # fused LM head on s2's rows (threshold rule, done list), own decode state
+        self.lm = make_lmhead_inputs(self.s2, 512)
+        self.lx = to_dev(self.lm.x, "bf16")
+        self.lwp = fd.lmhead_pack(torch.from_numpy(self.lm.w_codes).to(DEV).to(torch.bfloat16))
+        t3, m3 = make_decode_state(self.s2, [0, 20])  # sequence 0 has nothing left to decode
+        self.tk3_0, self.mk3_0 = torch.from_numpy(t3).to(DEV), torch.from_numpy(m3).to(DEV)
+        self.tk3, self.mk3 = self.tk3_0.clone(), self.mk3_0.clone()
+        self.nd3 = torch.zeros(b, dtype=torch.int32, device=DEV)
+        self.dp3 = torch.zeros((b, 32), dtype=torch.int32, device=DEV)
+        self.ds3 = torch.zeros(b, dtype=torch.int32, device=DEV)
+        self.nn3 = torch.zeros(1, dtype=torch.int32, device=DEV)
+        self.seq3 = seq_for(self.s2, True, self.keep)
+        self.lws = fd.new_workspace(fd.lmhead_unmask_workspace(self.seq3, 3000, 512))
 
     def restore(self):
         for dst, src in ((self.kc1, self.kc1_0), (self.vc1, self.vc1_0), (self.tk1, self.tk1_0),
                          (self.mk1, self.mk1_0), (self.tk2, self.tk2_0), (self.mk2, self.mk2_0),
-                         (self.bidx2, self.bidx2_0)):
+                         (self.bidx2, self.bidx2_0), (self.tk3, self.tk3_0), (self.mk3, self.mk3_0)):
             dst.copy_(src)
 
     def launch(self):
@@ -89,11 +104,14 @@ class _Step:
                             self.ds2, self.nn2, self.uws2, flags=fd.UNMASK_ADVANCE_BLOCK)
         fd.unmask_topk(self.seq1, self.lg1, 3, self.tk1, self.mk1, self.nd1, self.dp1, None, None, None,
                        self.uws1)
+        fd.lmhead_unmask_threshold(self.seq3, self.lx, self.lwp, 3000, 0.6, self.tk3, self.mk3, self.nd3, self.dp3,
+                                   None, self.ds3, self.nn3, self.lws)
 
     def outputs(self):
         return [t.clone() for t in (self.kc1, self.vc1, self.out1, self.out2, self.tk1, self.mk1, self.nd1,
                                     self.dp1, self.tk2, self.mk2, self.nd2, self.dp2, self.cf2, self.ds2,
-                                    self.nn2, self.bidx2)]
+                                    self.nn2, self.bidx2, self.tk3, self.mk3, self.nd3, self.dp3, self.ds3,
+                                    self.nn3)]
 
 
 def test_graph_replays_match_eager():
@@ -112,6 +130,16 @@ def test_graph_replays_match_eager():
     check_attn(ref[3].float().cpu().numpy().astype(np.float64), oracle_attn_subset(st.inp2, [1]), st.inp2,
                seqs=[1], label="graph step gqa")
     assert int(ref[14].item()) >= 1  # a sequence finished its block and is listed
+    # the fused LM head against the oracle: sequence 0 had nothing masked
+    from oracle import lmhead_unmask_ref
+    t3, m3 = st.tk3_0.cpu().numpy(), st.mk3_0.cpu().numpy()
+    r3 = lmhead_unmask_ref(st.lm.x, st.lm.weight(), t3, m3, st.s2.prompt_lens, st.s2.gen_len, 32,
+                           st.s2.block_idxs, threshold=0.6)
+    assert not r3.tie_step.any() and not r3.tie_tau.any()
+    assert np.array_equal(ref[16].cpu().numpy(), r3.tokens) and np.array_equal(ref[17].cpu().numpy(), r3.mask)
+    assert np.array_equal(ref[18].cpu().numpy(), r3.n_decoded) and int(r3.n_decoded[0]) == 0
+    assert int(ref[21].item()) == r3.n_done and list(ref[20].cpu().numpy()[:r3.n_done]) == list(r3.done_seqs)
+    assert 0 in list(r3.done_seqs)
 
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
