@@ -919,10 +919,20 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   constexpr int QPW = kGqaWaves;                    // query tiles per workgroup
   constexpr int SET = 2 * kTileBytes;               // ring set: one tile of K then V
   constexpr int DPR = 2;                            // 1 KB loads per wave per round
-  static_assert(NR >= 4 && NR <= 6, "the pipeline reads two ring sets per round; the epilogue needs 64 KB");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NR * SET];
+  static_assert(NR == 4, "four ring sets: the pipeline reads two per round; the epilogue needs 64 KB");
+  // One array per ring set: the compiler then tells the sets apart, so its
+  // LDS reads of one set are not held behind the LDS-DMA loads still in
+  // flight into another, and it schedules them like any LDS load.
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[SET];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[SET];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[SET];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[SET];
   auto set_ptr = [&](auto jc) __attribute__((always_inline)) -> uint8_t* {
-    return ring + (decltype(jc)::value % NR) * SET;
+    constexpr int J = decltype(jc)::value % NR;
+    if constexpr (J == 0) return ring0;
+    if constexpr (J == 1) return ring1;
+    if constexpr (J == 2) return ring2;
+    return ring3;
   };
 
   const int bid = blockIdx.x;
@@ -1042,27 +1052,17 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
       }
   }
 
+  // K operands as plain LDS loads and V^T operands with the transpose-read
+  // builtin: the compiler places and waits for them (lgkmcnt) itself.
   auto stage_s = [&](const uint8_t* tb) __attribute__((always_inline)) -> f32x16 {
-    const uint32_t base = lds_addr(tb);
-    uint32_t ad[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) ad[ks] = base + k_off[ks];
     bf16x8 kop[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kop[ks] = as_bf16x8(*(const uint4*)(tb + k_off[ks]));
     f32x16 S0, S1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) S0[r] = S1[r] = 0.f;
-    lds_read_b128_x4(ad, kop);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ks += 2) {
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 1], qop[ks + 1], S1, 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    lds_read_b128_x4(ad + 4, kop + 4);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 4; ks < 8; ks += 2) {
+    for (int ks = 0; ks < 8; ks += 2) {
       S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S0, 0, 0, 0);
       S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 1], qop[ks + 1], S1, 0, 0, 0);
     }
@@ -1071,26 +1071,17 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
 
   auto stage_pv = [&](const uint8_t* tb, int t0, f32x16 S) __attribute__((always_inline)) {
     bf16x8 vop[2][4];
-    {
-      const uint32_t base = lds_addr(tb);
-      uint32_t ad[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ad[e] = base + vt_off[e];
-      short4v tr[8];
-      __builtin_amdgcn_sched_barrier(0);
-      lds_read_tr16_x8<kTileBytes>(ad, tr);
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        __builtin_memcpy(&vop[0][dt], &tr[2 * dt], 8);
-        __builtin_memcpy((char*)&vop[0][dt] + 8, &tr[2 * dt + 1], 8);
+        typedef __attribute__((address_space(3))) short4v* LdsS4;
+        const uint8_t* vb = tb + kTileBytes + 16 * 256 * k2;
+        const short4v t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS4)(vb + vt_off[2 * dt]));
+        const short4v t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS4)(vb + vt_off[2 * dt + 1]));
+        __builtin_memcpy(&vop[k2][dt], &t0, 8);
+        __builtin_memcpy((char*)&vop[k2][dt] + 8, &t1, 8);
       }
-      lds_read_tr16_x8<kTileBytes + 16 * 256>(ad, tr);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        __builtin_memcpy(&vop[1][dt], &tr[2 * dt], 8);
-        __builtin_memcpy((char*)&vop[1][dt] + 8, &tr[2 * dt + 1], 8);
-      }
-    }
     if (t0 + kKT > g.ke) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -1158,7 +1149,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   if constexpr (NR > 5) issue(4, std::integral_constant<int, 4>{});
   wait_vm<(NR - 2) * DPR, true>();
   ring_barrier();
-  if (live) S_cur = stage_s(ring);
+  if (live) S_cur = stage_s(ring0);
   for (int q = 0; q < n_tiles; q += NR) {
     step(q, std::integral_constant<int, 0>{});
     step(q + 1, std::integral_constant<int, 1>{});
@@ -1194,7 +1185,9 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   // 2 q + hh of the 8 in the half, at chunk ^ (lq & 7)), so that each global
   // store writes 4 whole 256-byte rows... of the half: 4 x 128 bytes.
   float* part = a.part + ((((size_t)g.i * a.Hq + h) * a.n_qt + qt) * a.n_split + sp) * kPartFloats;
-  float* wbuf = (float*)(ring + wid * 8192);
+  // wave w: half w % 2 of ring set w / 2
+  uint8_t* wset = (wid >> 1) == 0 ? ring0 : (wid >> 1) == 1 ? ring1 : (wid >> 1) == 2 ? ring2 : ring3;
+  float* wbuf = (float*)(wset + (wid & 1) * 8192);
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     // head dims 64 hf + [0, 64): dt = 2 hf + dd
