@@ -7,6 +7,6 @@ from .fdllm import (  # noqa: F401
     BF16, F32, MODE, UNMASK_ADVANCE_BLOCK, FdllmError, SeqDesc, AttnDesc,
     attn_desc, block_attn, block_attn_workspace, kv_refresh, lib, lmhead_pack, lmhead_packed_bytes,
     lmhead_unmask_threshold, lmhead_unmask_topk, lmhead_unmask_workspace, new_workspace, seq_desc,
-    set_lmhead_tuning, set_timing_events, set_tuning, unmask_threshold, unmask_topk, unmask_workspace, version,
+    set_debug, set_lmhead_tuning, set_timing_events, set_tuning, unmask_threshold, unmask_topk, unmask_workspace, version,
     workspace_init,
 )

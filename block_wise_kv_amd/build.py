@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfdllm.so")
 
-SOURCES = ["fdllm_api.cpp", "block_attn.hip", "unmask.hip", "kv_refresh.hip", "lmhead.hip"]
+SOURCES = ["fdllm_api.cpp", "block_attn.hip", "unmask.hip", "kv_refresh.hip", "lmhead.hip", "validate.hip"]
 
 # Packed-fp32 VALU forms are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -1,9 +1,11 @@
 // Host side of the libfdllm C ABI: argument validation, workspace sizing,
 // grid planning and kernel dispatch.  No call allocates, synchronises or
 // touches the HIP runtime before its arguments have been validated.
+#include <limits.h>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -35,6 +37,39 @@ fdllm_status ok() {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Debug checks of device-resident arrays: FDLLM_DEBUG=1 in the environment
+// (read once) or fdllm_set_debug.
+int g_debug = -1;
+bool debug_on() {
+  if (g_debug < 0) {
+    const char* e = getenv("FDLLM_DEBUG");
+    g_debug = (e && atoi(e) != 0) ? 1 : 0;
+  }
+  return g_debug == 1;
+}
+
+// In debug mode, validate the device arrays a call is about to use (a
+// kernel, then a synchronisation of `stream`); FDLLM_OK otherwise.
+fdllm_status debug_validate(const SeqArgs& sa, int max_P, const int32_t* seq_ids, const int32_t* n_seq,
+                            void* stream) {
+  if (!debug_on() || (!sa.plens && !sa.bidx && !seq_ids && !n_seq)) return FDLLM_OK;
+  int key = INT_MAX;
+  hipError_t e = run_validate(sa, max_P, seq_ids, n_seq, (hipStream_t)stream, &key);
+  if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "debug validation failed: %s", hipGetErrorString(e));
+  if (key == INT_MAX) return FDLLM_OK;
+  const int idx = key / 8, code = key % 8;
+  switch (code) {
+    case VALIDATE_PROMPT:
+      return fail(FDLLM_ERR_INVALID_ARG, "prompt_lens[%d] outside [0, max_prompt_len %d]", idx, max_P);
+    case VALIDATE_BLOCK:
+      return fail(FDLLM_ERR_INVALID_ARG, "block_idxs[%d] outside [0, %d)", idx, sa.G / sa.B);
+    case VALIDATE_NSEQ:
+      return fail(FDLLM_ERR_INVALID_ARG, "n_seq outside [0, batch %d]", sa.b);
+    default:
+      return fail(FDLLM_ERR_INVALID_ARG, "seq_ids[%d] outside [0, batch %d)", idx, sa.b);
+  }
+}
 
 // Validate the sequence descriptor; fills `sa` and the host bounds.
 fdllm_status check_seq(const fdllm_seq_desc* s, SeqArgs& sa, int& max_P) {
@@ -221,6 +256,8 @@ fdllm_status run_lmhead_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t
     return fail(FDLLM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", su.ws,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(FDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  st = debug_validate(su.sa, su.max_P, nullptr, nullptr, stream);
+  if (st) return st;
   const LmheadPlan& p = su.plan;
   UnmaskArgs ua{};
   ua.sq = su.sa;
@@ -283,6 +320,12 @@ fdllm_status fdllm_set_tuning(int32_t attn_qt, int32_t attn_wgs, int32_t unmask_
   return ok();
 }
 
+fdllm_status fdllm_set_debug(int32_t on) {
+  if (on != 0 && on != 1) return fail(FDLLM_ERR_INVALID_ARG, "on must be 0 or 1 (got %d)", on);
+  g_debug = on;
+  return ok();
+}
+
 fdllm_status fdllm_set_timing_events(void* start_event, void* stop_event) {
   g_timing_start = (hipEvent_t)start_event;
   g_timing_stop = (hipEvent_t)stop_event;
@@ -322,6 +365,8 @@ fdllm_status fdllm_block_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(FDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   }
+  st = debug_validate(su.sa, su.max_P, nullptr, nullptr, stream);
+  if (st) return st;
   AttnArgs a{};
   a.sq = su.sa;
   a.mode = mode;
@@ -375,6 +420,8 @@ fdllm_status run_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits
     return fail(FDLLM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", su.ws,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(FDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  st = debug_validate(su.sa, su.max_P, nullptr, nullptr, stream);
+  if (st) return st;
   const size_t es = logits_dtype == FDLLM_BF16 ? 2 : 4;
   const bool vec = aligned16(logits) && ((size_t)row_stride * es) % 16 == 0 && ((size_t)seq_stride * es) % 16 == 0;
   UnmaskArgs a{};
@@ -511,6 +558,8 @@ fdllm_status fdllm_kv_refresh(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
       ranges_overlap(v_cache, cb, k_src, cb) || ranges_overlap(v_cache, cb, v_src, cb) ||
       ranges_overlap(k_cache, cb, v_cache, cb))
     return fail(FDLLM_ERR_INVALID_ARG, "caches must not alias the sources or each other");
+  st = debug_validate(sa, max_P, seq_ids, n_seq, stream);
+  if (st) return st;
   RefreshArgs a{};
   a.sq = sa;
   a.mode = mode;

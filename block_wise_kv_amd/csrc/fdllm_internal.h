@@ -169,6 +169,12 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, in
 // ------------------------------------------------------------------ misc
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
+// Debug-mode check of the device-resident per-sequence arrays (validate.hip):
+// key_out receives index * 8 + code of the first problem, or INT_MAX.
+enum { VALIDATE_PROMPT = 1, VALIDATE_BLOCK = 2, VALIDATE_NSEQ = 3, VALIDATE_SEQID = 4 };
+hipError_t run_validate(const SeqArgs& sq, int max_P, const int32_t* seq_ids, const int32_t* n_seq, hipStream_t st,
+                        int* key_out);
+
 // Measurement hook (fdllm_set_timing_events): returns the armed start/stop
 // events of the calling host thread (null when not armed) and disarms it.
 struct LaunchEvents {

@@ -82,6 +82,7 @@ _SIGS = [
     ("fdllm_kv_refresh", ctypes.c_int32,
      [ctypes.POINTER(SeqDesc), ctypes.POINTER(AttnDesc), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
     ("fdllm_workspace_init", ctypes.c_int32, [_P, ctypes.c_size_t, _P]),
+    ("fdllm_set_debug", ctypes.c_int32, [ctypes.c_int32]),
     ("fdllm_set_timing_events", ctypes.c_int32, [_P, _P]),
     ("fdllm_set_tuning", ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     ("fdllm_status_string", ctypes.c_char_p, [ctypes.c_int32]),
@@ -280,6 +281,11 @@ def kv_refresh(seq: SeqDesc, mode: str, k_src, v_src, k_cache, v_cache, seq_ids=
     ad = attn_desc(0, k_src.shape[2], k_src.shape[3], _dtype_code(k_src))
     _check(lib().fdllm_kv_refresh(ctypes.byref(seq), ctypes.byref(ad), MODE[mode], _ptr(k_src), _ptr(v_src),
                                   _ptr(k_cache), _ptr(v_cache), _ptr(seq_ids), _ptr(n_seq), _stream(stream)))
+
+
+def set_debug(on: bool):
+    """fdllm_set_debug: validate device-resident per-sequence arrays before each call."""
+    _check(lib().fdllm_set_debug(1 if on else 0))
 
 
 def set_timing_events(start_event, stop_event):

@@ -22,7 +22,10 @@
  *   - Host-side scalars and pointers are validated before any launch; on
  *     failure nothing is launched, an FDLLM_ERR_* code is returned and
  *     fdllm_last_error() describes it.  Device-resident per-sequence arrays
- *     (prompt_lens, block_idxs, seq_ids, n_seq) are trusted.
+ *     (prompt_lens, block_idxs, seq_ids, n_seq) are trusted, except in
+ *     debug mode (fdllm_set_debug, or FDLLM_DEBUG=1 in the environment):
+ *     then a validation kernel checks them and the call synchronises the
+ *     stream to read its verdict before launching anything else.
  *   - No exception or abort crosses the ABI.  Thread-safe: no global
  *     device state; fdllm_last_error() is per host thread.
  *   - Workspaces hold self-resetting counters: zero a workspace once with
@@ -272,6 +275,18 @@ fdllm_status fdllm_kv_refresh(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
 /* Zero a workspace (a fill kernel on `stream`; no memset node, so it can be
  * captured in a graph).  bytes must be a multiple of 4. */
 fdllm_status fdllm_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Debug mode (process-wide; initial value from the environment variable
+ * FDLLM_DEBUG): 1 = before its kernels, every call that reads device-
+ * resident per-sequence arrays checks them on the device -- 0 <=
+ * prompt_lens[i] <= max_prompt_len, 0 <= block_idxs[i] < gen_len /
+ * block_size, 0 <= *n_seq <= batch, 0 <= seq_ids[j] < batch for j < *n_seq
+ * -- then synchronises `stream` and returns FDLLM_ERR_INVALID_ARG (naming
+ * the first bad entry) without launching anything when one fails.  Not for
+ * use under stream capture; debug calls on one device must not overlap.
+ * 0 = the arrays are trusted (default).  FDLLM_ERR_INVALID_ARG for other
+ * values. */
+fdllm_status fdllm_set_debug(int32_t on);
 
 /* Measurement hook for profilers and benchmarks: the next kernel launched by
  * an fdllm_* call on this host thread records start_event when it begins and

@@ -247,3 +247,10 @@ def test_lmhead_sizes_and_pack_rejects():
     # one vocabulary tile per wave (the default for 32 rows) has twice the
     # workgroups (and partials) of two
     assert n1 == n and n1 > 1.9 * n2
+
+
+def test_set_debug_rejects():
+    L = fd.lib()
+    assert L.fdllm_set_debug(2) == 1 and "0 or 1" in L.fdllm_last_error().decode()
+    assert L.fdllm_set_debug(-1) == 1
+    assert L.fdllm_set_debug(0) == 0
