@@ -633,6 +633,7 @@ def main():
         "kernels": kernels,
         "large_copy_GB_per_s": round(copy_bps / 1e9, 1),
         "attn_unmask_block_steps_per_s": round(1.0 / t_au, 1),
+        "attn_unmask_sequence_block_steps_per_s": round(b.shape.batch / t_au, 1),
     }
     if not args.no_cpu_baseline and args.workload == "c2":
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
