@@ -93,23 +93,29 @@ __global__ __launch_bounds__(kLThreads, 1) void lmhead_kernel(LmheadArgs a) {
     return r;
   };
 
-  // hidden-state slots of this thread: slot q = j * 512 + tid of a phase
-  // buffer is lane q % 64 of B fragment q / 64 = s * RT + rt, i.e. row
-  // 32 rt + lane % 32, dims 16 s + 8 (lane / 32) + [0, 8) of the phase
+  // Hidden-state pieces of this thread, read row-major so that 8 lanes
+  // cover one 128-byte line: piece q = j * 512 + tid is dims 8 c + [0, 8) of
+  // row q / (KC / 8) of the workgroup's rows (c = q % (KC / 8)).  It belongs
+  // to B fragment (step c / 2, row tile), lane (row % 32) + 32 (c % 2); in
+  // LDS that lane's slot is XORed with (c % 16), which keeps the 8 writes
+  // of a line on distinct banks and each fragment 1 KB contiguous.
+  constexpr int PR = KC / 8;  // pieces per row and phase
   const uint16_t* xrow[PIECES];
   int koff[PIECES];
+  int slot[PIECES];
   bool rok[PIECES];
 #pragma unroll
   for (int j = 0; j < PIECES; ++j) {
     const int q = j * kLThreads + tid;
-    const int f = q >> 6, l = q & 63;
-    const int s = f / RT, rt = f - (f / RT) * RT;
-    const int r = row0 + rt * 32 + (l & 31);
+    const int rl = q / PR, c = q - (q / PR) * PR;
+    const int rt = rl >> 5, lane_f = (rl & 31) + 32 * (c & 1);
+    slot[j] = ((c >> 1) * RT + rt) * 64 + (lane_f ^ (c & 15));
+    const int r = row0 + rl;
     rok[j] = r < a.M;
     const int rr = rok[j] ? r : 0;
     const int i = rr / a.B, t = rr - (rr / a.B) * a.B;
     xrow[j] = a.x + (size_t)i * a.seq_stride + (size_t)t * a.row_stride;
-    koff[j] = 16 * s + 8 * (l >> 5);
+    koff[j] = 8 * c;
   }
   // Loads are unconditional and in bounds (clamped); slots of rows past the
   // batch or dims past the hidden size are zeroed with a mask applied when
@@ -125,8 +131,7 @@ __global__ __launch_bounds__(kLThreads, 1) void lmhead_kernel(LmheadArgs a) {
   auto store_h = [&](const uint4 (&hv)[PIECES], const uint32_t (&keep)[PIECES], int buf) {
 #pragma unroll
     for (int j = 0; j < PIECES; ++j)
-      s_h[buf * BUF + j * kLThreads + tid] =
-          make_uint4(hv[j].x & keep[j], hv[j].y & keep[j], hv[j].z & keep[j], hv[j].w & keep[j]);
+      s_h[buf * BUF + slot[j]] = make_uint4(hv[j].x & keep[j], hv[j].y & keep[j], hv[j].z & keep[j], hv[j].w & keep[j]);
   };
 
   f32x16 acc[VT][RT];
@@ -170,10 +175,12 @@ __global__ __launch_bounds__(kLThreads, 1) void lmhead_kernel(LmheadArgs a) {
       // is read one step ahead (8 row tiles have no registers for it: the
       // two waves of a SIMD hide each other's LDS latency instead).
       constexpr bool kAhead = RT <= 4;
+      // this lane's slot in the fragments of step s: lane ^ ((2 s + lane / 32) % 16)
+      auto bslot = [&](int s) { return lane ^ ((2 * s + (lane >> 5)) & 15); };
       bf16x8 bf[RT];
       if (kAhead) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) bf[rt] = as_bf16x8(hb[rt * 64 + lane]);
+        for (int rt = 0; rt < RT; ++rt) bf[rt] = as_bf16x8(hb[rt * 64 + bslot(0)]);
       }
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
@@ -181,10 +188,10 @@ __global__ __launch_bounds__(kLThreads, 1) void lmhead_kernel(LmheadArgs a) {
         bf16x8 bn[RT];
         if (!kAhead) {
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) bf[rt] = as_bf16x8(hb[(s * RT + rt) * 64 + lane]);
+          for (int rt = 0; rt < RT; ++rt) bf[rt] = as_bf16x8(hb[(s * RT + rt) * 64 + bslot(s)]);
         } else if (s + 1 < NKS) {
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) bn[rt] = as_bf16x8(hb[((s + 1) * RT + rt) * 64 + lane]);
+          for (int rt = 0; rt < RT; ++rt) bn[rt] = as_bf16x8(hb[((s + 1) * RT + rt) * 64 + bslot(s + 1)]);
         }
 #pragma unroll
         for (int v = 0; v < VT; ++v)
