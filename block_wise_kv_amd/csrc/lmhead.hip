@@ -24,7 +24,8 @@
 // Workgroup: 8 waves; each wave owns VT vocabulary tiles and every wave
 // multiplies them with the same RT row tiles (32 rows each) of hidden
 // states.  The hidden states are staged through LDS in phases of 512 / RT
-// hidden dims (two 32 KB buffers, laid out as B-operand fragments, one
+// hidden dims (128 at 8 row tiles; two buffers laid out as B-operand
+// fragments, read from global memory a whole line per 8 lanes, one
 // barrier per phase, no memory fence: the weight loads in flight are not
 // waited for).  Each wave keeps kLDepth MFMA steps of weight fragments in
 // flight across phase boundaries.  logits^T = W x^T: lane (c, h) of the
@@ -43,9 +44,12 @@ constexpr int kLWaves = 8;
 constexpr int kLThreads = kLWaves * 64;
 constexpr int kLDepth = 8;  // MFMA steps of weight fragments in flight per wave
 
+// Hidden dims per phase: 32 RT rows x KC dims x 2 bytes = 32 KB per buffer up
+// to 4 row tiles; at 8 row tiles 128 dims (64 KB per buffer, 8 MFMA steps
+// per phase: 4-step phases were measured 3-7 % slower).
 template <int RT>
 struct LPhase {
-  static constexpr int KC = 512 / RT;  // hidden dims per phase: 32 RT rows x KC dims x 2 bytes = 32 KB
+  static constexpr int KC = RT >= 8 ? 128 : 512 / RT;
 };
 
 template <int RT, int VT>
@@ -54,15 +58,16 @@ __global__ __launch_bounds__(kLThreads, 1) void lmhead_kernel(LmheadArgs a) {
   constexpr int NKS = KC / 16;             // MFMA steps per phase
   constexpr int BUF = NKS * RT * 64;       // 16-byte slots per phase buffer
   constexpr int PIECES = BUF / kLThreads;  // slots each thread fills per phase
-  // the window is a phase at most: at 8 row tiles (4 steps per phase) a
-  // window of 8 was measured slower (the LDS operand reads, not the weight
-  // stream, bound those shapes)
-  constexpr int D = kLDepth < NKS ? kLDepth : NKS;
+  constexpr int D = kLDepth;
+  static_assert(NKS % D == 0, "a phase holds whole prefetch windows (slot = step % D)");
   static_assert(BUF % kLThreads == 0, "phase buffer must split evenly over the threads");
+  // the two phase buffers; after the main loop the epilogue's per-wave
+  // partials reuse the same memory
   __shared__ uint4 s_h[2 * BUF];
-  __shared__ float s_m[kLWaves][RT * 32];
-  __shared__ int s_i[kLWaves][RT * 32];
-  __shared__ double s_z[kLWaves][RT * 32];
+  static_assert(kLWaves * RT * 32 * 16 <= 2 * BUF * 16, "epilogue partials must fit the phase buffers");
+  float(*s_m)[RT * 32] = reinterpret_cast<float(*)[RT * 32]>(s_h);
+  int(*s_i)[RT * 32] = reinterpret_cast<int(*)[RT * 32]>(s_m + kLWaves);
+  double(*s_z)[RT * 32] = reinterpret_cast<double(*)[RT * 32]>(s_i + kLWaves);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int bid = blockIdx.x;
@@ -155,15 +160,9 @@ __global__ __launch_bounds__(kLThreads, 1) void lmhead_kernel(LmheadArgs a) {
   wait_vm<63, true>();
   ring_barrier();
 
-  // PU phases per loop iteration, so that the prefetch window (D steps)
-  // maps onto fixed registers when a phase is shorter than the window
-  constexpr int PU = D > NKS ? D / NKS : 1;
-  static_assert(D % NKS == 0 || NKS % D == 0, "window and phase must nest");
-  for (int ph0 = 0; ph0 < nph; ph0 += PU) {
-#pragma unroll
-    for (int pu = 0; pu < PU; ++pu) {
-      const int ph = ph0 + pu;
-      const int buf = PU > 1 ? (pu & 1) : (ph & 1);  // PU is even when above 1
+  for (int ph = 0; ph < nph; ++ph) {
+    {
+      const int buf = ph & 1;
       // the next phase's hidden states, stored after this phase's steps
       uint4 hv[PIECES];
       uint32_t keep[PIECES];
@@ -184,7 +183,7 @@ __global__ __launch_bounds__(kLThreads, 1) void lmhead_kernel(LmheadArgs a) {
       }
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const int slot = (pu * NKS + s) % D;
+        const int slot = s % D;
         bf16x8 bn[RT];
         if (!kAhead) {
 #pragma unroll
