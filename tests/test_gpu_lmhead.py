@@ -218,3 +218,59 @@ def test_llada8b_b32_full_size_sampled():
     from workloads import shape_c4
     say("lmhead full size: LLaDA-8B b32 (sampled sequences)")
     _big_case(shape_c4(), 4096, tau=0.7, label="lmhead llada8b b32 tau0.7", seqs=[0, 13, 31])
+
+
+@pytest.mark.parametrize("rule", ["threshold", "topk"])
+def test_block_decode_loop_in_one_graph(rule):
+    # the in-block loop on the device: every step of a block (fused LM head +
+    # unmask, updating tokens and mask in place) captured in one HIP graph;
+    # each step's n_decoded equals the oracle's loop step by step and the
+    # final tokens and mask match (exact-grid logits, fixed across steps)
+    s = shape_custom("loop", "bf16", 2, 1, 1, 8, [10, 40], 96, 32, [1, 2], 3000, cfg_id=85)
+    inp = make_lmhead_inputs(s, 256)
+    tokens, mask = make_decode_state(s, [32, 17])
+    k = 3
+    n_steps = -(-32 // k) if rule == "topk" else 32
+    keep = []
+    from gpu_util import seq_for
+    seq = seq_for(s, True, keep)
+    x = to_dev(inp.x, "bf16")
+    wp = fd.lmhead_pack(lmhead_weight_dev(inp))
+    ws = fd.new_workspace(fd.lmhead_unmask_workspace(seq, s.vocab, 256))
+    tk = torch.from_numpy(tokens).to(DEV)
+    mk = torch.from_numpy(mask).to(DEV)
+    nd = torch.full((n_steps, 2), -7, dtype=torch.int32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for st in range(n_steps):
+                if rule == "topk":
+                    fd.lmhead_unmask_topk(seq, x, wp, s.vocab, k, tk, mk, nd[st], workspace=ws)
+                else:
+                    fd.lmhead_unmask_threshold(seq, x, wp, s.vocab, 0.6, tk, mk, nd[st], workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    tk.copy_(torch.from_numpy(tokens))
+    mk.copy_(torch.from_numpy(mask))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    # the oracle's loop on the same logits
+    w = inp.weight()
+    t_ref, m_ref = tokens, mask
+    per_step = []
+    for st in range(n_steps):
+        if rule == "topk":
+            r = lmhead_unmask_ref(inp.x, w, t_ref, m_ref, s.prompt_lens, s.gen_len, 32, s.block_idxs, k=k)
+        else:
+            r = lmhead_unmask_ref(inp.x, w, t_ref, m_ref, s.prompt_lens, s.gen_len, 32, s.block_idxs, threshold=0.6)
+        assert not r.tie_step.any() and not r.tie_tau.any(), f"near tie at step {st}"
+        t_ref, m_ref = r.tokens, r.mask
+        per_step.append(r.n_decoded)
+    got = nd.cpu().numpy()
+    assert np.array_equal(got, np.array(per_step)), (got.tolist(), np.array(per_step).tolist())
+    assert np.array_equal(tk.cpu().numpy(), t_ref) and np.array_equal(mk.cpu().numpy(), m_ref)
+    assert int(got.sum()) == 32 + 17
+    say(f"  in-graph {rule} loop: tokens per step {got[:, 0].tolist()} / {got[:, 1].tolist()}")
