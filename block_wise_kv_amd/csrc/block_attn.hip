@@ -58,6 +58,9 @@ constexpr int kKT = 32;                // keys per K/V tile
 constexpr int kD = 128;                // head dim (bf16 path)
 constexpr int kTileBytes = kKT * kD * 2;         // one K or V tile: 8 KB
 constexpr int kPartFloats = kQT * kD + 2 * kQT;  // one split partial: O, m, l
+// One split partial of the 8-wave ring: O as fp16 rows of 256 bytes, then
+// m, l and the rows' power-of-two scales in fp32.
+constexpr int kPart16Bytes = kQT * kD * 2 + 3 * kQT * 4;
 constexpr int kMaxSplit = 8;           // key chunks per group
 constexpr int kVtStride = 36;          // bf16 per d-row of the split kernel's transposed V tile
 // Split kernel's wave-merge buffer: [4 waves][32 query rows][32 chunks of 4
@@ -1180,44 +1183,103 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
     }
     return;
   }
-  // Partial (O, m, l) relative to the tile's exponent reference.  O goes
-  // through 8 KB of LDS per wave, 16 head dims at a time (row lq, chunk
-  // 2 q + hh of the 8 in the half, at chunk ^ (lq & 7)), so that each global
-  // store writes 4 whole 256-byte rows... of the half: 4 x 128 bytes.
-  float* part = a.part + ((((size_t)g.i * a.Hq + h) * a.n_qt + qt) * a.n_split + sp) * kPartFloats;
+  // Partial (O, m, l) relative to the tile's exponent reference, O in fp16
+  // with a power-of-two scale per query row (O = scale * stored): the row's
+  // largest |O| is stored in [2^14, 2^15), so no value overflows and every
+  // value keeps fp16's 11 significant bits, half the bytes of fp32.  O goes
+  // through 8 KB of LDS per wave so that each global store writes four whole
+  // 256-byte rows.
+  float amax = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(O[dt][r]));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 15;  // amax < 2^(e + 15)
+  uint8_t* part = (uint8_t*)a.part + (((((size_t)g.i * a.Hq + h) * a.n_qt + qt) * a.n_split + sp) * kPart16Bytes);
   // wave w: half w % 2 of ring set w / 2
   uint8_t* wset = (wid >> 1) == 0 ? ring0 : (wid >> 1) == 1 ? ring1 : (wid >> 1) == 2 ? ring2 : ring3;
-  float* wbuf = (float*)(wset + (wid & 1) * 8192);
+  uint8_t* wbuf = wset + (wid & 1) * 8192;
+  // lane (lq, hh) holds row lq, head dims 32 dt + 8 q4 + 4 hh + [0, 4): half
+  // of the row's 16-byte unit 4 dt + q4, placed at unit ^ (lq & 15)
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    // head dims 64 hf + [0, 64): dt = 2 hf + dd
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int k = 8 * dd + 2 * q4 + hh;  // chunk of 4 floats within the 64-dim half
-        const int dt = 2 * hf + dd;
-        *(float4*)(wbuf + (lq * 16 + (k ^ (lq & 15))) * 4) =
-            make_float4(O[dt][4 * q4], O[dt][4 * q4 + 1], O[dt][4 * q4 + 2], O[dt][4 * q4 + 3]);
-      }
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int row = 4 * v + (lane >> 4), k = lane & 15;
-      *(float4*)(part + row * kD + 64 * hf + 4 * k) = *(const float4*)(wbuf + (row * 16 + (k ^ (row & 15))) * 4);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      uint2 w;
+      w.x = pack_f16x2(__builtin_amdgcn_ldexpf(O[dt][4 * q4], -e), __builtin_amdgcn_ldexpf(O[dt][4 * q4 + 1], -e));
+      w.y = pack_f16x2(__builtin_amdgcn_ldexpf(O[dt][4 * q4 + 2], -e), __builtin_amdgcn_ldexpf(O[dt][4 * q4 + 3], -e));
+      *(uint2*)(wbuf + lq * 256 + 16 * ((4 * dt + q4) ^ (lq & 15)) + 8 * hh) = w;
     }
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int row = 4 * v + (lane >> 4), k = lane & 15;
+    *(uint4*)(part + row * 256 + 16 * k) = *(const uint4*)(wbuf + row * 256 + 16 * (k ^ (row & 15)));
   }
   if (hh == 0) {
-    part[kQT * kD + lq] = m_ref;
-    part[kQT * kD + kQT + lq] = l_col;
+    float* hdr = (float*)(part + kQT * kD * 2);
+    hdr[lq] = m_ref;
+    hdr[kQT + lq] = l_col;
+    hdr[2 * kQT + lq] = __builtin_amdgcn_ldexpf(1.f, e);
   }
 }
 
+// Merge NS fp16 key-chunk partials of one query tile (attn_gqa_kernel's
+// format; partial s starts at byte s * kPart16Bytes of resource r): query
+// row cq, head-dim columns c0 + 8 j + [0, 8), written to orow in bf16.  The
+// 8 lanes of a row read one whole 128-byte line per partial, and every load
+// is issued before any is used.
+template <int NS>
+__device__ __forceinline__ void merge_partials16_n(__amdgpu_buffer_rsrc_t r, int cq, int j, float c, uint16_t* orow,
+                                                   int c0) {
+  float ms[NS], ls[NS], ss[NS];
+  float4 xs[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int o = s * kPart16Bytes;
+    xs[s] = ld_coherent_b128(r, o + cq * kD * 2 + (c0 + 8 * j) * 2);
+    ms[s] = ld_coherent_b32(r, o + kQT * kD * 2 + cq * 4);
+    ls[s] = ld_coherent_b32(r, o + kQT * kD * 2 + (kQT + cq) * 4);
+    ss[s] = ld_coherent_b32(r, o + kQT * kD * 2 + (2 * kQT + cq) * 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float Mg = ms[0];
+#pragma unroll
+  for (int s = 1; s < NS; ++s) Mg = fmaxf(Mg, ms[s]);
+  float wsum = 0.f;
+  float ov[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ov[k] = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float w = exp2_fast((ms[s] - Mg) * c);
+    wsum += ls[s] * w;
+    const float ws = w * ss[s];
+    const uint32_t u[4] = {__float_as_uint(xs[s].x), __float_as_uint(xs[s].y), __float_as_uint(xs[s].z),
+                           __float_as_uint(xs[s].w)};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float lo, hi;
+      unpack_f16x2(u[k], lo, hi);
+      ov[2 * k] = fmaf(lo, ws, ov[2 * k]);
+      ov[2 * k + 1] = fmaf(hi, ws, ov[2 * k + 1]);
+    }
+  }
+  const float inv = 1.f / wsum;
+  uint4 w;
+  w.x = pack_bf16x2(ov[0] * inv, ov[1] * inv);
+  w.y = pack_bf16x2(ov[2] * inv, ov[3] * inv);
+  w.z = pack_bf16x2(ov[4] * inv, ov[5] * inv);
+  w.w = pack_bf16x2(ov[6] * inv, ov[7] * inv);
+  *(uint4*)(orow + c0 + 8 * j) = w;
+}
+
 // Merge the key-chunk partials written by attn_gqa_kernel in the launch
-// before: workgroup (query tile x 4 + column quarter, query head, sequence)
-// merges 32 head-dim columns of the tile's 32 rows, so the partial reads
-// spread over four times as many workgroups as query tiles.
+// before: workgroup (query tile x 2 + column half, query head, sequence)
+// merges 64 head-dim columns of the tile's 32 rows, so the partial reads
+// spread over twice as many workgroups as query tiles.
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
-  const int qt = blockIdx.x >> 2, quarter = blockIdx.x & 3, h = blockIdx.y, i = blockIdx.z;
+  const int qt = blockIdx.x >> 1, half = blockIdx.x & 1, h = blockIdx.y, i = blockIdx.z;
   const int P = seq_prompt(a.sq, i);
   const int L = P + a.sq.G;
   int a0, a1;
@@ -1226,21 +1288,22 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
   const int q0 = qt * kQT;
   if (q0 >= nq) return;
   const int n_act = __builtin_amdgcn_readfirstlane((L + a.kchunk - 1) / a.kchunk);
-  const auto r = make_rsrc(uniform_ptr(a.part + (((size_t)i * a.Hq + h) * a.n_qt + qt) * a.n_split * kPartFloats));
+  const auto r = make_rsrc(
+      uniform_ptr((const uint8_t*)a.part + (((size_t)i * a.Hq + h) * a.n_qt + qt) * a.n_split * kPart16Bytes));
   const int tid = threadIdx.x;
-  const int cq = tid >> 3, j = tid & 7, c0 = 32 * quarter;
+  const int cq = tid >> 3, j = tid & 7, c0 = 64 * half;
   if (q0 + cq >= nq) return;
   uint16_t* orow = (uint16_t*)a.out + (((size_t)i * a.fresh_rows + q0 + cq) * a.Hq + h) * kD;
   const float c = a.scale_log2;
   switch (n_act) {
-    case 1: merge_partials_n<1, 1>(r, cq, j, c, orow, c0); break;
-    case 2: merge_partials_n<2, 1>(r, cq, j, c, orow, c0); break;
-    case 3: merge_partials_n<3, 1>(r, cq, j, c, orow, c0); break;
-    case 4: merge_partials_n<4, 1>(r, cq, j, c, orow, c0); break;
-    case 5: merge_partials_n<5, 1>(r, cq, j, c, orow, c0); break;
-    case 6: merge_partials_n<6, 1>(r, cq, j, c, orow, c0); break;
-    case 7: merge_partials_n<7, 1>(r, cq, j, c, orow, c0); break;
-    default: merge_partials_n<8, 1>(r, cq, j, c, orow, c0); break;
+    case 1: merge_partials16_n<1>(r, cq, j, c, orow, c0); break;
+    case 2: merge_partials16_n<2>(r, cq, j, c, orow, c0); break;
+    case 3: merge_partials16_n<3>(r, cq, j, c, orow, c0); break;
+    case 4: merge_partials16_n<4>(r, cq, j, c, orow, c0); break;
+    case 5: merge_partials16_n<5>(r, cq, j, c, orow, c0); break;
+    case 6: merge_partials16_n<6>(r, cq, j, c, orow, c0); break;
+    case 7: merge_partials16_n<7>(r, cq, j, c, orow, c0); break;
+    default: merge_partials16_n<8>(r, cq, j, c, orow, c0); break;
   }
 }
 
@@ -1390,7 +1453,8 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   p.grid = p.per_xcd * 8;
   if (ns > 1) {
     const size_t slots = (size_t)b * Hq * p.n_qt * ns;
-    p.part_bytes = ((slots * kPartFloats * sizeof(float)) + 255) & ~(size_t)255;
+    const size_t slot_bytes = QT == 8 ? (size_t)kPart16Bytes : kPartFloats * sizeof(float);
+    p.part_bytes = ((slots * slot_bytes) + 255) & ~(size_t)255;
     // arrival counters for the in-kernel merge (the 8-tile ring is merged by
     // a second kernel and needs none)
     const size_t counters = QT == 1 ? (size_t)b * Hq * p.n_qt : QT == 8 ? 0 : (size_t)base;
@@ -1423,7 +1487,7 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, in
       if (p.n_split == 1) return launch_kernel(kern, grid, gblock, 0, st, ev.start, ev.stop, a);
       const hipError_t e = launch_kernel(kern, grid, gblock, 0, st, ev.start, (hipEvent_t) nullptr, a);
       if (e != hipSuccess) return e;
-      const dim3 mgrid((unsigned)p.n_qt * 4, (unsigned)a.Hq, (unsigned)a.sq.b);
+      const dim3 mgrid((unsigned)p.n_qt * 2, (unsigned)a.Hq, (unsigned)a.sq.b);
       return launch_kernel(attn_merge_kernel, mgrid, block, 0, st, (hipEvent_t) nullptr, ev.stop, a);
     }
     if (p.qt_per_wg == 4) return launch_kernel(attn_ring_kernel<4, 4>, grid, block, 0, st, ev.start, ev.stop, a);

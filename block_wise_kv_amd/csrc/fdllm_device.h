@@ -28,6 +28,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Two floats as IEEE fp16 (round to nearest even) in one word, low first,
+// and back.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 v = {(_Float16)lo, (_Float16)hi};
+  uint32_t u;
+  __builtin_memcpy(&u, &v, 4);
+  return u;
+}
+__device__ __forceinline__ void unpack_f16x2(uint32_t u, float& lo, float& hi) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 v;
+  __builtin_memcpy(&v, &u, 4);
+  lo = (float)v.x;
+  hi = (float)v.y;
+}
+
 // 16 bytes as the 8 bf16 values of an MFMA operand.
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;

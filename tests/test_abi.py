@@ -175,8 +175,9 @@ def test_set_tuning_rejects_and_replans():
     finally:
         fd.set_tuning()
     assert one == 0 and many > 0  # one key chunk needs no partials
-    # 8 key chunks of fp32 partials (O, m, l per row) for 8 x 28 heads x 32 rows
-    assert one8 == 0 and auto8 == 8 * 28 * 8 * (32 * 128 + 64) * 4
+    # 8 key chunks of partials for 8 x 28 heads x 32 rows: O in fp16 (256 bytes
+    # per row), then m, l and the row scale in fp32
+    assert one8 == 0 and auto8 == 8 * 28 * 8 * (32 * 128 * 2 + 3 * 32 * 4)
 
 
 def _lm_call(seq, vocab=126464, hidden=4096, x=P1, ss=None, rs=None, wp=P2, tau=0.9, k=None, flags=0, ws=P7,

@@ -162,3 +162,30 @@ def test_kernel_variants(case, qt, wgs):
         fd.set_tuning()
     check_attn(out, _full(inp), inp, label=f"{name} qt={qt} wgs={wgs}")
     assert np.array_equal(outs[0], outs[1], equal_nan=True)
+
+
+@pytest.mark.parametrize("qt", [1, 2, 4, 8])
+def test_output_scales_exactly_with_v(qt):
+    # Attention is linear in V, and scaling V by 2^e scales every product,
+    # sum and stored partial by 2^e exactly (the 8-wave ring stores its split
+    # partials in fp16 with a power-of-two scale per row), so the output must
+    # scale bit-exactly: at 2^40 an unscaled fp16 partial would overflow, at
+    # 2^-40 it would flush to zero.
+    import block_wise_kv_amd as fd
+    from dataclasses import replace
+    s = shape_custom("scale", "bf16", 3, 14, 2, 128, [37, 100, 5], 96, 32, [0, 2, 1], 64, cfg_id=53)
+    inp = make_attn_inputs(s, "dual")
+    fd.set_tuning(attn_qt=qt, attn_wgs=4096)
+    try:
+        base, _, _ = run_attn(inp, ragged=True)
+        for e in (40, -40):
+            f = 2.0 ** e
+            sc = replace(inp, v_new=inp.v_new * f, v_cache=inp.v_cache * f)
+            got, _, _ = run_attn(sc, ragged=True)
+            live = ~np.isnan(base)
+            assert np.array_equal(np.isnan(got), ~live)
+            assert np.array_equal(got[live], base[live] * f), f"qt={qt}: output at V * 2^{e} is not 2^{e} times the output"
+    finally:
+        fd.set_tuning()
+    check_attn(base, _full(inp), inp, label=f"scale qt={qt}")
+    say(f"  qt={qt}: outputs at V * 2^40 and V * 2^-40 equal the scaled output bit for bit")
