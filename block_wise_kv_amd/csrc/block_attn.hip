@@ -234,6 +234,81 @@ __device__ __forceinline__ void merge_partials(int n, __amdgpu_buffer_rsrc_t r, 
   }
 }
 
+// Merge NS key-chunk partials of one query tile in the fp16 format (O rows
+// of 256 bytes in fp16, then m, l and the rows' power-of-two scales in
+// fp32; partial s starts at byte s * kPart16Bytes of resource r): query row
+// cq, head-dim columns c0 + 64 h + 8 j + [0, 8) for h = 0..NH-1, written to
+// orow in bf16.  The 8 lanes of a row read one whole 128-byte line per
+// partial and half, and every load is issued before any is used, so the
+// merge costs one memory round trip.
+template <int NS, int NH>
+__device__ __forceinline__ void merge_partials16_n(__amdgpu_buffer_rsrc_t r, int cq, int j, float c, uint16_t* orow,
+                                                   int c0) {
+  float ms[NS], ls[NS], ss[NS];
+  float4 xs[NS][NH];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int o = s * kPart16Bytes;
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) xs[s][hf] = ld_coherent_b128(r, o + cq * kD * 2 + (c0 + 64 * hf + 8 * j) * 2);
+    ms[s] = ld_coherent_b32(r, o + kQT * kD * 2 + cq * 4);
+    ls[s] = ld_coherent_b32(r, o + kQT * kD * 2 + (kQT + cq) * 4);
+    ss[s] = ld_coherent_b32(r, o + kQT * kD * 2 + (2 * kQT + cq) * 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float Mg = ms[0];
+#pragma unroll
+  for (int s = 1; s < NS; ++s) Mg = fmaxf(Mg, ms[s]);
+  float wsum = 0.f;
+  float ov[NH][8];
+#pragma unroll
+  for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ov[hf][k] = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float w = exp2_fast((ms[s] - Mg) * c);
+    wsum += ls[s] * w;
+    const float ws = w * ss[s];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      const uint32_t u[4] = {__float_as_uint(xs[s][hf].x), __float_as_uint(xs[s][hf].y), __float_as_uint(xs[s][hf].z),
+                             __float_as_uint(xs[s][hf].w)};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float lo, hi;
+        unpack_f16x2(u[k], lo, hi);
+        ov[hf][2 * k] = fmaf(lo, ws, ov[hf][2 * k]);
+        ov[hf][2 * k + 1] = fmaf(hi, ws, ov[hf][2 * k + 1]);
+      }
+    }
+  }
+  const float inv = 1.f / wsum;
+#pragma unroll
+  for (int hf = 0; hf < NH; ++hf) {
+    uint4 w;
+    w.x = pack_bf16x2(ov[hf][0] * inv, ov[hf][1] * inv);
+    w.y = pack_bf16x2(ov[hf][2] * inv, ov[hf][3] * inv);
+    w.z = pack_bf16x2(ov[hf][4] * inv, ov[hf][5] * inv);
+    w.w = pack_bf16x2(ov[hf][6] * inv, ov[hf][7] * inv);
+    *(uint4*)(orow + c0 + 64 * hf + 8 * j) = w;
+  }
+}
+// n (wave-uniform, 1..kMaxSplit) partials of whole rows: only those are read.
+__device__ __forceinline__ void merge_partials16(int n, __amdgpu_buffer_rsrc_t r, int cq, int j, float c,
+                                                 uint16_t* orow) {
+  switch (n) {
+    case 1: merge_partials16_n<1, 2>(r, cq, j, c, orow, 0); break;
+    case 2: merge_partials16_n<2, 2>(r, cq, j, c, orow, 0); break;
+    case 3: merge_partials16_n<3, 2>(r, cq, j, c, orow, 0); break;
+    case 4: merge_partials16_n<4, 2>(r, cq, j, c, orow, 0); break;
+    case 5: merge_partials16_n<5, 2>(r, cq, j, c, orow, 0); break;
+    case 6: merge_partials16_n<6, 2>(r, cq, j, c, orow, 0); break;
+    case 7: merge_partials16_n<7, 2>(r, cq, j, c, orow, 0); break;
+    default: merge_partials16_n<8, 2>(r, cq, j, c, orow, 0); break;
+  }
+}
+
 // ------------------------------------------------------------------ bf16 MFMA, split keys
 // One query tile per workgroup (MHA with a single query tile per head):
 // the 4 waves take alternate 32-key sub-tiles of the workgroup's key chunk,
@@ -432,15 +507,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
     }
   __syncthreads();
 
-  // thread (oq, j) sums head dims 32 v + 4 j + [0, 4), v = 0..3, of query
-  // row oq over the waves: the 8 lanes of a row cover whole 128-byte lines
+  // thread (oq, j) sums head dims 8 j + [0, 8) and 64 + 8 j + [0, 8) of
+  // query row oq over the waves (chunks 2 j, 2 j + 1, 16 + 2 j, 17 + 2 j):
+  // the 8 lanes of a row then cover whole 128-byte lines of the fp16
+  // partial and of the bf16 output
   const bool split = a.n_split > 1;
   const size_t slot = (((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt) * a.n_split + g.s;  // (i, h, qt, s)
   const int oq = tid >> 3, oj = tid & 7;
   float4 o[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int k = 8 * v + oj;
+    const int k = 16 * (v >> 1) + 2 * oj + (v & 1);
     float4 acc = *(const float4*)(red + (oq * 32 + (k ^ red_swizzle(oq))) * 4);
 #pragma unroll
     for (int w = 1; w < 4; ++w) {
@@ -457,32 +534,53 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
       const float inv = 1.f / s_L[oq];
       uint16_t* orow = (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + oq) * a.Hq + g.h) * kD;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        uint2 w;
-        w.x = pack_bf16x2(o[v].x * inv, o[v].y * inv);
-        w.y = pack_bf16x2(o[v].z * inv, o[v].w * inv);
-        *(uint2*)(orow + 32 * v + 4 * oj) = w;
+      for (int hf = 0; hf < 2; ++hf) {
+        const float4 x = o[2 * hf], y = o[2 * hf + 1];
+        uint4 w;
+        w.x = pack_bf16x2(x.x * inv, x.y * inv);
+        w.y = pack_bf16x2(x.z * inv, x.w * inv);
+        w.z = pack_bf16x2(y.x * inv, y.y * inv);
+        w.w = pack_bf16x2(y.z * inv, y.w * inv);
+        *(uint4*)(orow + 64 * hf + 8 * oj) = w;
       }
     }
     return;
   }
-  const auto prs = make_rsrc(a.part + slot * kPartFloats);
+  // Partial (O, m, l) in attn_gqa_kernel's format: O in fp16 with a
+  // power-of-two scale per row, the row's largest |O| stored in [2^14, 2^15).
+  float amax = 0.f;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) st_coherent_b128(prs, (oq * kD + 32 * v + 4 * oj) * 4, o[v]);
-
+  for (int v = 0; v < 4; ++v)
+    amax = fmaxf(fmaxf(amax, fmaxf(fabsf(o[v].x), fabsf(o[v].y))), fmaxf(fabsf(o[v].z), fabsf(o[v].w)));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 15;
+  const auto prs = make_rsrc((uint8_t*)a.part + slot * kPart16Bytes);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const float4 x = o[2 * hf], y = o[2 * hf + 1];
+    u32x4 w;
+    w.x = pack_f16x2(__builtin_amdgcn_ldexpf(x.x, -e), __builtin_amdgcn_ldexpf(x.y, -e));
+    w.y = pack_f16x2(__builtin_amdgcn_ldexpf(x.z, -e), __builtin_amdgcn_ldexpf(x.w, -e));
+    w.z = pack_f16x2(__builtin_amdgcn_ldexpf(y.x, -e), __builtin_amdgcn_ldexpf(y.y, -e));
+    w.w = pack_f16x2(__builtin_amdgcn_ldexpf(y.z, -e), __builtin_amdgcn_ldexpf(y.w, -e));
+    __builtin_amdgcn_raw_buffer_store_b128(w, prs, oq * kD * 2 + 128 * hf + 16 * oj, 0, kCoherentAux);
+  }
+  if (oj == 0) st_coherent_b32(prs, kQT * kD * 2 + (2 * kQT + oq) * 4, __builtin_amdgcn_ldexpf(1.f, e));
   if (wid == 0 && hh == 0) {
-    st_coherent_b32(prs, (kQT * kD + lq) * 4, M);
-    st_coherent_b32(prs, (kQT * kD + kQT + lq) * 4, Lsum);
+    st_coherent_b32(prs, kQT * kD * 2 + lq * 4, M);
+    st_coherent_b32(prs, kQT * kD * 2 + (kQT + lq) * 4, Lsum);
   }
   uint32_t* cnt = a.cnt + ((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt;
   if (!block_arrive(cnt, (unsigned)g.n_act, &s_last)) return;
 
   // ---- last workgroup of this tile: merge the n_act split partials
-  const auto r = make_rsrc(uniform_ptr(a.part + (slot - g.s) * kPartFloats));
+  const auto r = make_rsrc(uniform_ptr((const uint8_t*)a.part + (slot - g.s) * kPart16Bytes));
   const int cq = tid >> 3;            // query row
   if (q0 + cq < g.nq)
-    merge_partials(__builtin_amdgcn_readfirstlane(g.n_act), r, cq, tid & 7, c,
-                   (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + cq) * a.Hq + g.h) * kD);
+    merge_partials16(__builtin_amdgcn_readfirstlane(g.n_act), r, cq, tid & 7, c,
+                     (uint16_t*)a.out + (((size_t)g.i * a.fresh_rows + q0 + cq) * a.Hq + g.h) * kD);
   if (tid == 0) *cnt = 0u;
 }
 
@@ -1224,56 +1322,6 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   }
 }
 
-// Merge NS fp16 key-chunk partials of one query tile (attn_gqa_kernel's
-// format; partial s starts at byte s * kPart16Bytes of resource r): query
-// row cq, head-dim columns c0 + 8 j + [0, 8), written to orow in bf16.  The
-// 8 lanes of a row read one whole 128-byte line per partial, and every load
-// is issued before any is used.
-template <int NS>
-__device__ __forceinline__ void merge_partials16_n(__amdgpu_buffer_rsrc_t r, int cq, int j, float c, uint16_t* orow,
-                                                   int c0) {
-  float ms[NS], ls[NS], ss[NS];
-  float4 xs[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int o = s * kPart16Bytes;
-    xs[s] = ld_coherent_b128(r, o + cq * kD * 2 + (c0 + 8 * j) * 2);
-    ms[s] = ld_coherent_b32(r, o + kQT * kD * 2 + cq * 4);
-    ls[s] = ld_coherent_b32(r, o + kQT * kD * 2 + (kQT + cq) * 4);
-    ss[s] = ld_coherent_b32(r, o + kQT * kD * 2 + (2 * kQT + cq) * 4);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  float Mg = ms[0];
-#pragma unroll
-  for (int s = 1; s < NS; ++s) Mg = fmaxf(Mg, ms[s]);
-  float wsum = 0.f;
-  float ov[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) ov[k] = 0.f;
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const float w = exp2_fast((ms[s] - Mg) * c);
-    wsum += ls[s] * w;
-    const float ws = w * ss[s];
-    const uint32_t u[4] = {__float_as_uint(xs[s].x), __float_as_uint(xs[s].y), __float_as_uint(xs[s].z),
-                           __float_as_uint(xs[s].w)};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float lo, hi;
-      unpack_f16x2(u[k], lo, hi);
-      ov[2 * k] = fmaf(lo, ws, ov[2 * k]);
-      ov[2 * k + 1] = fmaf(hi, ws, ov[2 * k + 1]);
-    }
-  }
-  const float inv = 1.f / wsum;
-  uint4 w;
-  w.x = pack_bf16x2(ov[0] * inv, ov[1] * inv);
-  w.y = pack_bf16x2(ov[2] * inv, ov[3] * inv);
-  w.z = pack_bf16x2(ov[4] * inv, ov[5] * inv);
-  w.w = pack_bf16x2(ov[6] * inv, ov[7] * inv);
-  *(uint4*)(orow + c0 + 8 * j) = w;
-}
-
 // Merge the key-chunk partials written by attn_gqa_kernel in the launch
 // before: workgroup (query tile x 2 + column half, query head, sequence)
 // merges 64 head-dim columns of the tile's 32 rows, so the partial reads
@@ -1296,14 +1344,14 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
   uint16_t* orow = (uint16_t*)a.out + (((size_t)i * a.fresh_rows + q0 + cq) * a.Hq + h) * kD;
   const float c = a.scale_log2;
   switch (n_act) {
-    case 1: merge_partials16_n<1>(r, cq, j, c, orow, c0); break;
-    case 2: merge_partials16_n<2>(r, cq, j, c, orow, c0); break;
-    case 3: merge_partials16_n<3>(r, cq, j, c, orow, c0); break;
-    case 4: merge_partials16_n<4>(r, cq, j, c, orow, c0); break;
-    case 5: merge_partials16_n<5>(r, cq, j, c, orow, c0); break;
-    case 6: merge_partials16_n<6>(r, cq, j, c, orow, c0); break;
-    case 7: merge_partials16_n<7>(r, cq, j, c, orow, c0); break;
-    default: merge_partials16_n<8>(r, cq, j, c, orow, c0); break;
+    case 1: merge_partials16_n<1, 1>(r, cq, j, c, orow, c0); break;
+    case 2: merge_partials16_n<2, 1>(r, cq, j, c, orow, c0); break;
+    case 3: merge_partials16_n<3, 1>(r, cq, j, c, orow, c0); break;
+    case 4: merge_partials16_n<4, 1>(r, cq, j, c, orow, c0); break;
+    case 5: merge_partials16_n<5, 1>(r, cq, j, c, orow, c0); break;
+    case 6: merge_partials16_n<6, 1>(r, cq, j, c, orow, c0); break;
+    case 7: merge_partials16_n<7, 1>(r, cq, j, c, orow, c0); break;
+    default: merge_partials16_n<8, 1>(r, cq, j, c, orow, c0); break;
   }
 }
 
@@ -1453,7 +1501,7 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   p.grid = p.per_xcd * 8;
   if (ns > 1) {
     const size_t slots = (size_t)b * Hq * p.n_qt * ns;
-    const size_t slot_bytes = QT == 8 ? (size_t)kPart16Bytes : kPartFloats * sizeof(float);
+    const size_t slot_bytes = (QT == 8 || QT == 1) ? (size_t)kPart16Bytes : kPartFloats * sizeof(float);
     p.part_bytes = ((slots * slot_bytes) + 255) & ~(size_t)255;
     // arrival counters for the in-kernel merge (the 8-tile ring is merged by
     // a second kernel and needs none)
