@@ -1154,23 +1154,22 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   }
 
   // K operands as plain LDS loads and V^T operands with the transpose-read
-  // builtin: the compiler places and waits for them (lgkmcnt) itself.
-  auto stage_s = [&](const uint8_t* tb) __attribute__((always_inline)) -> f32x16 {
+  // builtin: the compiler waits for them (lgkmcnt) itself.  All eight K
+  // reads go out before the first product (the empty asm statements keep
+  // the compiler from interleaving them with the products), so their
+  // latency is paid once, and the eight products accumulate in one chain.
+  auto stage_s = [&](const uint8_t* tb, f32x16& S) __attribute__((always_inline)) {
     bf16x8 kop[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kop[ks] = as_bf16x8(*(const uint4*)(tb + k_off[ks]));
-    f32x16 S0, S1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S0[r] = S1[r] = 0.f;
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(kop[ks]));
+    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qop[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-    for (int ks = 0; ks < 8; ks += 2) {
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 1], qop[ks + 1], S1, 0, 0, 0);
-    }
-    return S0 + S1;
+    for (int ks = 1; ks < 8; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S, 0, 0, 0);
   };
 
-  auto stage_pv = [&](const uint8_t* tb, int t0, f32x16 S) __attribute__((always_inline)) {
+  auto stage_pv = [&](const uint8_t* tb, int t0, f32x16& S) __attribute__((always_inline)) {
     bf16x8 vop[2][4];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
@@ -1227,19 +1226,17 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
 
   // the LDS ring kernel's pipeline with one tile per round: step q waits
   // until tile q + 1 is in, meets at the barrier, refills the set tile
-  // q - 1 used, starts S^T of tile q + 1 and finishes tile q
-  f32x16 S_cur;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) S_cur[r] = 0.f;
+  // q - 1 used, starts S^T of tile q + 1 and finishes tile q.  S^T of tile
+  // q sits in Sb[q % 2] (the loop body has an even number of steps, so the
+  // index is known at compile time and nothing is copied).
+  f32x16 Sb[2] = {f32x16{}, f32x16{}};
   auto step = [&](int q, auto jc) __attribute__((always_inline)) {
     constexpr int J = decltype(jc)::value;
     wait_vm<(NR - 3) * DPR, true>();
     ring_barrier();
     issue(q + NR - 1, std::integral_constant<int, (J + NR - 1) % NR>{});
-    f32x16 S_nxt = S_cur;
-    if (live && q + 1 < n_tiles) S_nxt = stage_s(set_ptr(std::integral_constant<int, (J + 1) % NR>{}));
-    if (live && q < n_tiles) stage_pv(set_ptr(jc), g.kb + q * kKT, S_cur);
-    S_cur = S_nxt;
+    if (live && q + 1 < n_tiles) stage_s(set_ptr(std::integral_constant<int, (J + 1) % NR>{}), Sb[(J + 1) & 1]);
+    if (live && q < n_tiles) stage_pv(set_ptr(jc), g.kb + q * kKT, Sb[J & 1]);
   };
   issue(0, std::integral_constant<int, 0>{});
 #pragma unroll
@@ -1250,7 +1247,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   if constexpr (NR > 5) issue(4, std::integral_constant<int, 4>{});
   wait_vm<(NR - 2) * DPR, true>();
   ring_barrier();
-  if (live) S_cur = stage_s(ring0);
+  if (live) stage_s(ring0, Sb[0]);
   for (int q = 0; q < n_tiles; q += NR) {
     step(q, std::integral_constant<int, 0>{});
     step(q + 1, std::integral_constant<int, 1>{});
@@ -1441,8 +1438,8 @@ void set_attn_tuning(int qt, int wgs) {
 // Kernel and work split (see the choice of QT below).  The key split fills
 // the GPU when there are few work items.  The environment
 // variables FDLLM_ATTN_QT (1: split-key kernel, 2, 4: LDS ring, 8: LDS ring
-// with two query tiles per wave) and FDLLM_ATTN_TARGET_WGS override the
-// defaults for tuning.
+// with 8 waves of one query tile each) and FDLLM_ATTN_TARGET_WGS override
+// the defaults for tuning.
 AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max) {
   (void)d;
   AttnPlan p{};
@@ -1464,9 +1461,9 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   // across the heads of a GQA group would need a key split whose merge
   // costs more than the shared loads save).  Several query tiles per head
   // (prefix / no cache): the ring, four query tiles per K/V tile.
-  // A GQA group of 4 or more heads with one query tile each: the ring with
-  // two query tiles per wave (8 per workgroup), so the group's heads share
-  // every K/V tile.
+  // A GQA group of 4 or more heads with one query tile each: the 8-wave
+  // ring (8 query tiles per workgroup), so the group's heads share every K/V
+  // tile.
   if (QT != 1 && QT != 2 && QT != 4 && QT != 8) QT = p.n_qt == 1 ? (g >= 4 ? 8 : 1) : (T >= 4 ? 4 : 2);
   p.qt_per_wg = QT;
   static const long target_env = env_long("FDLLM_ATTN_TARGET_WGS", 0);

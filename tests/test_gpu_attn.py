@@ -148,7 +148,7 @@ VARIANTS = [
 @pytest.mark.parametrize("case", VARIANTS, ids=lambda c: c[0])
 def test_kernel_variants(case, qt, wgs):
     # every attention kernel (split-key, LDS ring with 2 or 4 query tiles per
-    # workgroup, LDS ring with 2 per wave) and key split on the same inputs
+    # workgroup, 8-wave LDS ring with one per wave) and key split on the same inputs
     import block_wise_kv_amd as fd
     name, dt, b, hq, hkv, d, P, G, B, k, mode = case
     s = shape_custom(name, dt, b, hq, hkv, d, P, G, B, k, 64, cfg_id=52)
