@@ -30,10 +30,12 @@
 // With QT = 4 every wave owns one query tile and consumes every K/V tile;
 // with QT = 2 or 1 the 2 or 4 waves of a query tile take alternate tiles
 // and merge (max, sum, O) through LDS at the end.  When the keys are split
-// over several workgroups, each publishes fp32 partials with agent-scope
-// (write-through) 16-byte stores and bumps a counter; the last one to arrive
-// reads every partial with agent-scope loads, merges them and writes the
-// output, then resets the counter.
+// over several workgroups, each publishes its partial (O, m, l: fp32 here,
+// fp16 O with a power-of-two row scale in the split-key kernel and the
+// 8-wave ring) with agent-scope (write-through) 16-byte stores and bumps a
+// counter; the last one to arrive reads every partial with agent-scope
+// loads, merges them and writes the output, then resets the counter (the
+// 8-wave ring leaves the merge to a second kernel).
 //
 // Work items are ordered so that the groups sharing a KV head (and key
 // chunk) are adjacent, and the grid is remapped so adjacent items land on
