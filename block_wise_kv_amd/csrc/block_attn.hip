@@ -425,7 +425,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
       if (key >= g.ke) S[r] = -INFINITY;
       mx = fmaxf(mx, S[r]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xor_combine<32>(mx, [](float x, float y) { return fmaxf(x, y); });
     const float m_new = fmaxf(m_run, mx);
     const float alpha = exp2_fast((m_run - m_new) * c);
     const float mc = m_new * c;
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
   }
 
   // ---- merge the 4 waves (per query column lq)
-  const float l_full = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_full = xor_combine<32>(l_run, [](float x, float y) { return x + y; });
   if (hh == 0) {
     s_m[wid][lq] = m_run;
     s_l[wid][lq] = l_full;
@@ -554,9 +554,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
   for (int v = 0; v < 4; ++v)
     amax = fmaxf(fmaxf(amax, fmaxf(fabsf(o[v].x), fabsf(o[v].y))), fmaxf(fabsf(o[v].z), fabsf(o[v].w)));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+  amax = xor_combine<1>(amax, [](float x, float y) { return fmaxf(x, y); });
+  amax = xor_combine<2>(amax, [](float x, float y) { return fmaxf(x, y); });
+  amax = xor_combine<4>(amax, [](float x, float y) { return fmaxf(x, y); });
   const int e = __builtin_amdgcn_frexp_expf(amax) - 15;
   const auto prs = make_rsrc((uint8_t*)a.part + slot * kPart16Bytes);
 #pragma unroll
@@ -830,7 +830,7 @@ __global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_r
     float mx = S[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xor_combine<32>(mx, [](float x, float y) { return fmaxf(x, y); });
     // The exponent reference m_ref moves only when some column's max passes
     // it by more than kRefSlack (log2 units): p <= 2^kRefSlack stays well
     // inside bf16 and fp32 range, and the accumulator is rarely rescaled.
@@ -916,7 +916,7 @@ __global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_r
   ring_barrier();
 
   // ---- combine the R key phases of each query tile (per column lq)
-  const float l_col = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_col = xor_combine<32>(l_run, [](float x, float y) { return x + y; });
   float M = m_ref, Lsum = l_col;
   if constexpr (R > 1) {
     if (hh == 0) {
@@ -1194,7 +1194,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
     float mx = S[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xor_combine<32>(mx, [](float x, float y) { return fmaxf(x, y); });
     if (__ballot((mx - m_ref) * c > kRefSlack)) {
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = exp2_fast((m_ref - m_new) * c);
@@ -1262,7 +1262,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   ring_barrier();
   if (!live) return;
 
-  const float l_col = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_col = xor_combine<32>(l_run, [](float x, float y) { return x + y; });
   if (a.n_split == 1) {
     // lane holds column q0 + lq, head-dim 32 dt + 8 (r / 4) + 4 hh + [0, 4)
     if (q0 + lq < g.nq) {
@@ -1291,7 +1291,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(O[dt][r]));
-  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  amax = xor_combine<32>(amax, [](float x, float y) { return fmaxf(x, y); });
   const int e = __builtin_amdgcn_frexp_expf(amax) - 15;  // amax < 2^(e + 15)
   uint8_t* part = (uint8_t*)a.part + (((((size_t)g.i * a.Hq + h) * a.n_qt + qt) * a.n_split + sp) * kPart16Bytes);
   // wave w: half w % 2 of ring set w / 2

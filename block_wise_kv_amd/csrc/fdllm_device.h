@@ -74,26 +74,84 @@ __device__ __forceinline__ void ring_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Wave64 reductions.
+// ---- cross-lane exchange without LDS (gfx950).  lane_pair<O>(v, a, b)
+// sets {a, b} = {v of this lane, v of lane ^ O}, in an order that depends
+// only on the lane: O = 1, 2 by DPP quad permutations, 4 and 8 by DPP row
+// shifts and a select, 16 and 32 by v_permlane16_swap / v_permlane32_swap
+// (which hand both lanes of a pair the same two values).  Every use
+// combines a and b with a commutative operation, so both lanes of a pair
+// end with the same bits, as with a butterfly through LDS.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int O>
+__device__ __forceinline__ void lane_pair_u32(uint32_t v, uint32_t& a, uint32_t& b) {
+  static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16 || O == 32, "lane offset");
+  if constexpr (O == 1 || O == 2) {
+    a = v;
+    b = dpp_u32<O == 1 ? 0xB1 : 0x4E>(v);  // quad_perm [1,0,3,2] / [2,3,0,1]
+  } else if constexpr (O == 4 || O == 8) {
+    const uint32_t lo = dpp_u32<0x110 + O>(v);  // row_shr:O, lane - O
+    const uint32_t hi = dpp_u32<0x100 + O>(v);  // row_shl:O, lane + O
+    a = v;
+    b = (__lane_id() & O) ? lo : hi;
+  } else if constexpr (O == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  }
+}
+template <int O, typename T>
+__device__ __forceinline__ void lane_pair(T v, T& a, T& b) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    uint32_t x, y;
+    lane_pair_u32<O>(__builtin_bit_cast(uint32_t, v), x, y);
+    a = __builtin_bit_cast(T, x);
+    b = __builtin_bit_cast(T, y);
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    uint32_t al, bl, ah, bh;
+    lane_pair_u32<O>((uint32_t)u, al, bl);
+    lane_pair_u32<O>((uint32_t)(u >> 32), ah, bh);
+    a = __builtin_bit_cast(T, ((uint64_t)ah << 32) | al);
+    b = __builtin_bit_cast(T, ((uint64_t)bh << 32) | bl);
+  }
+}
+// v combined with lane (lane ^ O)'s v by a commutative op.
+template <int O, typename T, typename F>
+__device__ __forceinline__ T xor_combine(T v, F op) {
+  T a, b;
+  lane_pair<O>(v, a, b);
+  return op(a, b);
+}
+
+// Wave64 reductions (every lane gets the result).
+template <typename T, typename F>
+__device__ __forceinline__ T wave_reduce(T v, F op) {
+  v = xor_combine<32>(v, op);
+  v = xor_combine<16>(v, op);
+  v = xor_combine<8>(v, op);
+  v = xor_combine<4>(v, op);
+  v = xor_combine<2>(v, op);
+  return xor_combine<1>(v, op);
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, [](float x, float y) { return x + y; });
 }
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, [](double x, double y) { return x + y; });
 }
 __device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](int x, int y) { return min(x, y); });
 }
 
 // ---- cross-workgroup publication without cache write-back / invalidate.

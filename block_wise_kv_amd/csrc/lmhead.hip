@@ -242,13 +242,17 @@ __global__ __launch_bounds__(kLThreads, 1) void lmhead_kernel(LmheadArgs a) {
 #pragma unroll
       for (int n = 0; n < w; ++n) e[n] += e[n + w];
     float z = (m == -INFINITY) ? 0.f : e[0];
-    const float m2 = __shfl_xor(m, 32, 64);
-    const float z2 = __shfl_xor(z, 32, 64);
-    const int i2 = __shfl_xor(idx, 32, 64);
-    const float M = fmaxf(m, m2);
-    const float za = (m == -INFINITY) ? 0.f : z * exp2_fast((m - M) * kLog2e);
+    // the two half-waves hold the same rows: (m1, z1, i1) and (m2, z2, i2)
+    // are this lane's and lane ^ 32's, in a lane-pair order
+    float m1, m2, z1, z2;
+    int i1, i2;
+    lane_pair<32>(m, m1, m2);
+    lane_pair<32>(z, z1, z2);
+    lane_pair<32>(idx, i1, i2);
+    const float M = fmaxf(m1, m2);
+    const float za = (m1 == -INFINITY) ? 0.f : z1 * exp2_fast((m1 - M) * kLog2e);
     const float zb = (m2 == -INFINITY) ? 0.f : z2 * exp2_fast((m2 - M) * kLog2e);
-    const int I = min(m == M ? idx : INT_MAX, m2 == M ? i2 : INT_MAX);
+    const int I = min(m1 == M ? i1 : INT_MAX, m2 == M ? i2 : INT_MAX);
     if (lane < 32) {
       s_m[wid][rt * 32 + lane] = M;
       s_z[wid][rt * 32 + lane] = (double)za + (double)zb;

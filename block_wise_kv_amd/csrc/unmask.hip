@@ -218,6 +218,25 @@ __device__ __forceinline__ void best_of(double& c, int& t, double c2, int t2) {
     t = t2;
   }
 }
+// (c, t) <- the better of this lane's and lane ^ O's (best_of is symmetric)
+template <int O>
+__device__ __forceinline__ void best_of_lanes(double& c, int& t) {
+  double c1, c2;
+  int t1, t2;
+  lane_pair<O>(c, c1, c2);
+  lane_pair<O>(t, t1, t2);
+  c = c1;
+  t = t1;
+  best_of(c, t, c2, t2);
+}
+__device__ __forceinline__ void best_of_wave(double& c, int& t) {
+  best_of_lanes<32>(c, t);
+  best_of_lanes<16>(c, t);
+  best_of_lanes<8>(c, t);
+  best_of_lanes<4>(c, t);
+  best_of_lanes<2>(c, t);
+  best_of_lanes<1>(c, t);
+}
 
 // Per-sequence finalisation by the last workgroup of sequence i.  Rows are
 // handled 256 at a time, one per thread; a row's mask byte and every chunk
@@ -251,8 +270,7 @@ __device__ void unmask_finalize_wave(const UnmaskArgs& a, int i, int start, cons
   const int n_masked = __popcll(bal_m);
   double bc = mk ? conf : -1.0;
   int bt = mk ? t : INT_MAX;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) best_of(bc, bt, __shfl_xor(bc, o, 64), __shfl_xor(bt, o, 64));
+  best_of_wave(bc, bt);
   const bool fallback = bal_p == 0 && n_masked > 0;
   uint64_t bal_s = fallback ? (bt < 64 ? (1ull << bt) : 0ull) : bal_p;
   if (a.topk > 0) {
@@ -330,9 +348,13 @@ __device__ void unmask_finalize_wave(const UnmaskArgs& a, int i, int start, cons
   }
   if (!want_list) return;
   // the last sequence to finish writes the ascending list of finished ones
-  const uint64_t old_all = __shfl(old, 0, 64);
+  const auto lane0 = [](uint64_t v) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), 0) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 0);
+  };
+  const uint64_t old_all = lane0(old);
   if ((int)(old_all >> 48) != b - 1) return;
-  const uint64_t bits = (old_all + __shfl(add, 0, 64)) & ((1ull << 48) - 1ull);
+  const uint64_t bits = (old_all + lane0(add)) & ((1ull << 48) - 1ull);
   const bool fl = t < b && ((bits >> t) & 1ull);
   const uint64_t bal = __ballot(fl);
   if (fl && a.done_seqs) a.done_seqs[__popcll(bal & ((1ull << t) - 1ull))] = t;
@@ -387,11 +409,11 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start, const Row
     n_masked += msk[p];
     n_pass += msk[p] && conf[p] > tau;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    n_masked += __shfl_xor(n_masked, o, 64);
-    n_pass += __shfl_xor(n_pass, o, 64);
-    best_of(bc, bt, __shfl_xor(bc, o, 64), __shfl_xor(bt, o, 64));
+  {
+    const auto add = [](int x, int y) { return x + y; };
+    n_masked = wave_reduce(n_masked, add);
+    n_pass = wave_reduce(n_pass, add);
+    best_of_wave(bc, bt);
   }
   if (lane == 0) {
     s_cnt[wid][0] = n_masked;
@@ -598,14 +620,21 @@ __global__ __launch_bounds__(kUT) void unmask_kernel(UnmaskArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       masked = __builtin_amdgcn_readfirstlane(mv) != 0;
       const int n_run = masked ? n_it : 1;
+      // va holds iteration it and vb iteration it + 1.  The last one or two
+      // iterations are reduced after the loop, so no load is issued that
+      // only the code after the loop would wait for (its registers are
+      // reused there); at most one half-iteration of clamped loads past the
+      // chunk is in flight, issued before the last reduction.
       int it = 0;
-      do {
+      while (it + 2 < n_run) {
         reduce(va, it);
         load(va, it + 2);
-        if (it + 1 < n_run) reduce(vb, it + 1);
+        reduce(vb, it + 1);
         load(vb, it + 3);
         it += 2;
-      } while (it < n_run);
+      }
+      reduce(va, it);
+      if (it + 1 < n_run) reduce(vb, it + 1);
     } else {
       masked = load_mask_byte(mptr) != 0;  // no full vector: only the scalar tail below
     }
@@ -733,12 +762,27 @@ __global__ __launch_bounds__(NT) void lmhead_finalize_kernel(UnmaskArgs a, const
           if (c0 + tpr * u < nv) merge_partial(M, Z, I, q[u].m, q[u].z, q[u].idx);
       }
     }
-    for (int o = 1; o < tpr; o <<= 1) {
-      const float m2 = __shfl_xor(M, o, 64);
-      const double z2 = __shfl_xor(Z, o, 64);
-      const int i2 = __shfl_xor(I, o, 64);
-      merge_partial(M, Z, I, m2, z2, i2);
-    }
+    // merge the tpr lanes of a row (merge_partial is symmetric)
+    const auto merge_lanes = [&](auto oc) __attribute__((always_inline)) {
+      constexpr int O = decltype(oc)::value;
+      if (O < tpr) {
+        float m1, m2;
+        double z1, z2;
+        int i1, i2;
+        lane_pair<O>(M, m1, m2);
+        lane_pair<O>(Z, z1, z2);
+        lane_pair<O>(I, i1, i2);
+        M = m1;
+        Z = z1;
+        I = i1;
+        merge_partial(M, Z, I, m2, z2, i2);
+      }
+    };
+    merge_lanes(std::integral_constant<int, 1>{});
+    merge_lanes(std::integral_constant<int, 2>{});
+    merge_lanes(std::integral_constant<int, 4>{});
+    merge_lanes(std::integral_constant<int, 8>{});
+    merge_lanes(std::integral_constant<int, 16>{});
     if (t < B && j == 0) {
       s_z[t] = Z;
       s_tok[t] = I;
