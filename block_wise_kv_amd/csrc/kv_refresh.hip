@@ -16,8 +16,9 @@
 namespace fdllm {
 
 constexpr int kRefreshThreads = 256;
-constexpr int kRefreshVPT = 4;  // vectors of K (and of V) per thread
 
+// VPT: vectors of K (and of V) per thread
+template <int VPT>
 __global__ __launch_bounds__(kRefreshThreads) void kv_refresh_kernel(RefreshArgs a) {
   int i = blockIdx.y;
   if (a.seq_ids) {
@@ -37,19 +38,19 @@ __global__ __launch_bounds__(kRefreshThreads) void kv_refresh_kernel(RefreshArgs
   u32x4* kd = (u32x4*)a.k_cache + (size_t)i * seq_vecs;
   u32x4* vd = (u32x4*)a.v_cache + (size_t)i * seq_vecs;
 
-  const uint32_t base = blockIdx.x * (kRefreshThreads * kRefreshVPT) + threadIdx.x;
+  const uint32_t base = blockIdx.x * (kRefreshThreads * VPT) + threadIdx.x;
   if (nvec == 0) return;
   // loads are unconditional (clamped to the last vector), so all of a
   // thread's loads are in flight together; only the stores are guarded
-  u32x4 kv[kRefreshVPT], vv[kRefreshVPT];
+  u32x4 kv[VPT], vv[VPT];
 #pragma unroll
-  for (int u = 0; u < kRefreshVPT; ++u) {
+  for (int u = 0; u < VPT; ++u) {
     const uint32_t v = min(base + u * kRefreshThreads, nvec - 1u);
     kv[u] = __builtin_nontemporal_load(ks + v);
     vv[u] = __builtin_nontemporal_load(vs + v);
   }
 #pragma unroll
-  for (int u = 0; u < kRefreshVPT; ++u) {
+  for (int u = 0; u < VPT; ++u) {
     const uint32_t v = base + u * kRefreshThreads;
     if (v < nvec) {
       const uint32_t c = v & vpr_mask;
@@ -63,14 +64,31 @@ __global__ __launch_bounds__(kRefreshThreads) void kv_refresh_kernel(RefreshArgs
   }
 }
 
+// Vectors per thread: the choice that gives the least work to the busiest
+// CU when the workgroups are dealt evenly over 256 CUs (4 unless the
+// refresh fits in about one round: 6 for the LLaDA-8B single-sequence
+// refresh, one workgroup per CU instead of one or two).
 hipError_t launch_kv_refresh(const RefreshArgs& a, int max_rows, hipStream_t st) {
   const size_t nvec = ((size_t)max_rows * a.Hkv) << a.row_vec_shift;
-  const size_t per_block = (size_t)kRefreshThreads * kRefreshVPT;
+  if (nvec == 0) return hipSuccess;
+  const int cand[3] = {4, 6, 3};
+  int vpt = 4;
+  size_t best = ~(size_t)0;
+  for (int k = 0; k < 3; ++k) {
+    const size_t per_block = (size_t)kRefreshThreads * cand[k];
+    const size_t wgs = ((nvec + per_block - 1) / per_block) * (size_t)a.sq.b;
+    const size_t cost = ((wgs + 255) / 256) * (size_t)cand[k];
+    if (cost < best) {
+      best = cost;
+      vpt = cand[k];
+    }
+  }
+  const size_t per_block = (size_t)kRefreshThreads * vpt;
   const unsigned gx = (unsigned)((nvec + per_block - 1) / per_block);
-  if (gx == 0) return hipSuccess;
   dim3 grid(gx, (unsigned)a.sq.b, 1);
   const LaunchEvents ev = take_launch_events();
-  return launch_kernel(kv_refresh_kernel, grid, dim3(kRefreshThreads), 0, st, ev.start, ev.stop, a);
+  auto* kern = vpt == 6 ? kv_refresh_kernel<6> : vpt == 3 ? kv_refresh_kernel<3> : kv_refresh_kernel<4>;
+  return launch_kernel(kern, grid, dim3(kRefreshThreads), 0, st, ev.start, ev.stop, a);
 }
 
 // ------------------------------------------------------------------ zero fill

@@ -10,7 +10,7 @@ from gpu_util import (DEV, check_attn, compare_unmask, oracle_attn_subset, requi
                       seq_for, to_dev)
 from oracle import attn_ref, refresh_ref, unmask_ref
 from workloads import (AttnInputs, make_attn_inputs, make_decode_state, make_logits, make_refresh_src,
-                       n_masked_c5, shape_c1, shape_c3, shape_c5, shape_custom)
+                       n_masked_c5, shape_c1, shape_c2, shape_c3, shape_c5, shape_custom)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +43,9 @@ CASES = [
     ("c1", shape_c1(), False),
     ("ragged_bf16", shape_custom("rr", "bf16", 3, 4, 2, 128, [37, 100, 5], 96, 32, [0, 2, 1], 64, cfg_id=70), True),
     ("f32_d64", shape_custom("rf", "f32", 2, 4, 3, 64, [12, 4], 32, 8, [1, 3], 64, cfg_id=71), True),
+    # one LLaDA-8B sequence: the launch with 6 vectors per thread (one
+    # workgroup per CU); the cases above take 3, the Dream-7B tests 4
+    ("c2_llada", shape_c2(), False),
 ]
 
 
