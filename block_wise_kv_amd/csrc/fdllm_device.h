@@ -131,6 +131,15 @@ __device__ __forceinline__ T xor_combine(T v, F op) {
   return op(a, b);
 }
 
+// Workgroup barrier for data exchanged through LDS only: it waits for this
+// wave's LDS operations, not for its global loads still in flight (which
+// __syncthreads' full fence would).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wave64 reductions (every lane gets the result).
 template <typename T, typename F>
 __device__ __forceinline__ T wave_reduce(T v, F op) {

@@ -155,9 +155,9 @@ __device__ __forceinline__ void fold(RowAcc& acc, float* x, int it) {
 __device__ float block_max(float v, float* s_f) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   v = wave_max(v);
-  __syncthreads();
+  lds_sync();
   if (lane == 0) s_f[wid] = v;
-  __syncthreads();
+  lds_sync();
   float r = s_f[0];
 #pragma unroll
   for (int w = 1; w < kUWaves; ++w) r = fmaxf(r, s_f[w]);
@@ -167,12 +167,12 @@ __device__ void block_sum_min(double z, int idx, double* s_d, int* s_i, double& 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   z = wave_sum_d(z);
   idx = wave_min_i(idx);
-  __syncthreads();
+  lds_sync();
   if (lane == 0) {
     s_d[wid] = z;
     s_i[wid] = idx;
   }
-  __syncthreads();
+  lds_sync();
   z_out = s_d[0];
   idx_out = s_i[0];
 #pragma unroll
