@@ -78,9 +78,10 @@ __device__ __forceinline__ void ring_barrier() {
 // sets {a, b} = {v of this lane, v of lane ^ O}, in an order that depends
 // only on the lane: O = 1, 2 by DPP quad permutations, 4 and 8 by DPP row
 // shifts and a select, 16 and 32 by v_permlane16_swap / v_permlane32_swap
-// (which hand both lanes of a pair the same two values).  Every use
-// combines a and b with a commutative operation, so both lanes of a pair
-// end with the same bits, as with a butterfly through LDS.
+// (each swaps rows of 16 or halves of 32 lanes between two copies of v, so
+// the two results hold both lanes' values).  Every use combines a and b
+// with a commutative operation, so both lanes of a pair end with the same
+// bits, as with a butterfly through LDS.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
