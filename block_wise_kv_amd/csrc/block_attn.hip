@@ -772,27 +772,15 @@ __global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_r
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) ad[ks] = base + k_off[ks];
     bf16x8 kop[8];
-    // two accumulation chains, so consecutive products do not wait on each
-    // other; the second half of K is read while the first half multiplies
-    f32x16 S0, S1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S0[r] = S1[r] = 0.f;
+    // all eight K reads before the products (one LDS wait), then one
+    // accumulation chain (no final sum of two)
     lds_read_b128_x4(ad, kop);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < 4; ks += 2) {
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 1], qop[ks + 1], S1, 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
     lds_read_b128_x4(ad + 4, kop + 4);
     __builtin_amdgcn_sched_barrier(0);
+    f32x16 S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qop[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-    for (int ks = 4; ks < 8; ks += 2) {
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks + 1], qop[ks + 1], S1, 0, 0, 0);
-    }
-    return S0 + S1;
+    for (int ks = 1; ks < 8; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S, 0, 0, 0);
+    return S;
   };
 
   // Softmax of S (keys t0..t0+31, V at tb + 8 KB) and O^T += V^T P^T.
