@@ -139,7 +139,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Four 16-byte LDS reads at addr[i], completed before the block ends (see
-// lds_read_tr16_x8 for why the ring's reads are hidden from the compiler).
+// lds_read_tr16_x16 for why the ring's reads are hidden from the compiler).
 __device__ __forceinline__ void lds_read_b128_x4(const uint32_t* addr, bf16x8* o) {
   asm volatile(
       "ds_read_b128 %0, %4\n\t"
@@ -151,27 +151,38 @@ __device__ __forceinline__ void lds_read_b128_x4(const uint32_t* addr, bf16x8* o
       : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]));
 }
 
-// Eight transpose reads (ds_read_b64_tr_b16) at addr[i] + OFF, completed
-// before the block ends.  The ring's LDS reads are asm blocks with their own
+// Sixteen transpose reads (ds_read_b64_tr_b16) at addr[i] + OFF0 and
+// addr[i] + OFF1 (both halves of a V tile), completed before the block ends:
+// the loads' destinations are valid only after the wait, so it sits in the
+// same asm statement.  The ring's LDS reads are asm blocks with their own
 // wait: the compiler does not see them, so it does not order them after the
 // ring's LDS loads still in flight into other sets (it would wait for every
 // load in flight); the explicit counter waits and barriers of the ring loop
 // order them instead.
-template <int OFF>
-__device__ __forceinline__ void lds_read_tr16_x8(const uint32_t (&addr)[8], short4v (&o)[8]) {
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void lds_read_tr16_x16(const uint32_t (&addr)[8], short4v (&o)[8], short4v (&p)[8]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
-      "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %2, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %4, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %6, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %12, %20 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]),
+        "=&v"(p[0]), "=&v"(p[1]), "=&v"(p[2]), "=&v"(p[3]), "=&v"(p[4]), "=&v"(p[5]), "=&v"(p[6]), "=&v"(p[7])
       : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
-        "v"(addr[7]), "i"(OFF));
+        "v"(addr[7]), "i"(OFF0), "i"(OFF1));
 }
 
 // Merge the NS key-chunk partials (O, m, l in fp32) of one query tile, whose
@@ -792,19 +803,15 @@ __global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_r
       uint32_t ad[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) ad[e] = base + vt_off[e];
-      short4v t[8];
+      short4v t[8], t2[8];
       __builtin_amdgcn_sched_barrier(0);
-      lds_read_tr16_x8<kTileBytes>(ad, t);
+      lds_read_tr16_x16<kTileBytes, kTileBytes + 16 * 256>(ad, t, t2);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         __builtin_memcpy(&vop[0][dt], &t[2 * dt], 8);
         __builtin_memcpy((char*)&vop[0][dt] + 8, &t[2 * dt + 1], 8);
-      }
-      lds_read_tr16_x8<kTileBytes + 16 * 256>(ad, t);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        __builtin_memcpy(&vop[1][dt], &t[2 * dt], 8);
-        __builtin_memcpy((char*)&vop[1][dt] + 8, &t[2 * dt + 1], 8);
+        __builtin_memcpy(&vop[1][dt], &t2[2 * dt], 8);
+        __builtin_memcpy((char*)&vop[1][dt] + 8, &t2[2 * dt + 1], 8);
       }
     }
     // lane holds query column lq, keys t0 + 8 (r / 4) + 4 hh + (r % 4)
