@@ -138,17 +138,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-// Four 16-byte LDS reads at addr[i], completed before the block ends (see
+// Eight 16-byte LDS reads at addr[i], completed before the block ends (see
 // lds_read_tr16_x16 for why the ring's reads are hidden from the compiler).
-__device__ __forceinline__ void lds_read_b128_x4(const uint32_t* addr, bf16x8* o) {
+__device__ __forceinline__ void lds_read_b128_x8(const uint32_t* addr, bf16x8* o) {
   asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\t"
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]));
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+        "v"(addr[7]));
 }
 
 // Sixteen transpose reads (ds_read_b64_tr_b16) at addr[i] + OFF0 and
@@ -785,8 +790,7 @@ __global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_r
     bf16x8 kop[8];
     // all eight K reads before the products (one LDS wait), then one
     // accumulation chain (no final sum of two)
-    lds_read_b128_x4(ad, kop);
-    lds_read_b128_x4(ad + 4, kop + 4);
+    lds_read_b128_x8(ad, kop);
     __builtin_amdgcn_sched_barrier(0);
     f32x16 S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qop[0], f32x16{}, 0, 0, 0);
 #pragma unroll
