@@ -1,31 +1,45 @@
 #!/usr/bin/env python3
 """Benchmark of the Fast-dLLM block-decoding hot path on one MI355X.
 
-Workload: one LLaDA-8B-shaped layer, batch 1, 32 heads x 128 (MHA), prompt
-512 + gen 256, block size 32, DualCache, block index swept 0..7, thresholds
-cycled over {0.7, 0.9, 1.0}.  One step = for each of the 8 block indices:
-the block-boundary cache refresh (fdllm_kv_refresh), the block attention
-(fdllm_block_attn) and the threshold unmask over the 126464-wide vocabulary
-(fdllm_unmask_threshold) -- every part of the hot path once per block-step.
-Inputs are seeded synthetic tensors already resident in HBM.
+Default workload: the ragged Dream-7B batch -- 64 sequences, 28 query / 4
+KV heads x 128, prompt lengths U(256, 4096) per sequence, gen 512, block 32,
+block index U{0..15} per sequence, U{1..32} masked block rows per sequence,
+DualCache, vocabulary 152064, threshold 0.7 on calibrated confidences (each
+masked row's top probability u ~ U(0.5, 1), so a step decodes several
+tokens per sequence and some blocks finish, as in real decoding; the
+literal peak recipe falls back to one token per row and, at this seed,
+finishes no block).  One step is one full decoding
+step of the 28-layer model's hot path: the block attention of every layer
+(fdllm_block_attn over that layer's own cache), one threshold unmask over
+the batch with block advance (fdllm_unmask_threshold), then the cache
+refresh of every sequence whose block is finished, in every layer
+(fdllm_kv_refresh from the device-side done list).  Inputs are seeded
+synthetic tensors already resident in HBM (34 GB: each layer owns its
+caches, refresh sources and fresh rows, so nothing is served from the
+256 MB Infinity Cache); every step starts from the same decoding state (its
+own copies of tokens, mask and block indices).
 
-To measure HBM and not the 256 MB Infinity Cache, buffers rotate over 32
-layer sets (caches and refresh sources, 806 MB) and 48 logits sets (389 MB);
-the refresh of a block-step writes the layer set 16 positions away from the
-one its attention reads.  Each unmask call gets its own pristine token/mask
-pair, so every step sees the first step after a refresh (all 32 block
-positions masked).
+value = layer block-steps per second = 28 x steps / elapsed: each layer's
+block attention counts as one block-step, with the step's single unmask and
+its refresh amortised over the 28 layers (the reading of "block-steps/s per
+layer (attn + unmask)" for a whole model step).  Beside it:
+attn_unmask_block_steps_per_s = 1 / (t_attn + t_unmask) per call, the
+sequence rates (times the batch) and the refresh reported on its own.
 
 The K timed steps are captured once in a HIP graph and replayed between two
 device synchronisations.  Per-kernel durations come from a second pass over
-the same K steps in which every kernel is launched with its own start/stop
+the same K steps in which every call is launched with its own start/stop
 HIP events (libfdllm's timing hook, hipExtLaunchKernel), on the stream it
-runs on.
+runs on.  The fp64 oracle is timed on the host's cores (all of them, then
+one thread) on one layer of the same step, scaled to the full step.
 
---workload selects other shapes for measuring the kernels (Dream-7B GQA
-DualCache and prefix cache, large-batch LLaDA-8B); the default is the one
-above.  Prints one JSON line.  --gpus N > 1 is refused: this path runs on one
-GPU.
+--workload selects other shapes for measuring the kernels (c2: LLaDA-8B b1
+DualCache swept over block index 0..7, c3 / c3p: Dream-7B b8 DualCache /
+prefix cache, c4: LLaDA-8B b32).  --sweep-block-size times attention and
+unmask of the large-batch LLaDA-8B layer at block sizes 4..128;
+--sweep-tau decodes its blocks at thresholds 0.5..1.0 and counts the tokens
+decoded per step.  Prints one JSON line.  --gpus N > 1 is refused: this path
+runs on one GPU.
 
 --lmhead measures the step before the unmask instead: the vocabulary
 projection fused with the confidence pass (fdllm_lmhead_unmask_threshold,
@@ -49,9 +63,15 @@ PEAK_HBM_BPS = 8.0e12
 N_BLOCKS = 8                 # block indices of the LLaDA-8B workload (CPU baseline)
 TAUS = (0.7, 0.9, 1.0)
 
-# Workloads.  The default (c2) is the configuration the metric is quoted on;
-# the others exist for measuring the kernels at the other shapes.
+# Workloads.  The default (c5, the largest single-GPU configuration) is
+# measured by c5_main; the others exist for measuring the kernels at the
+# other shapes.
 WORKLOADS = {
+    "c5": dict(desc="Ragged Dream-7B batch: 64 sequences, 28 q / 4 kv heads x 128, prompt U(256, 4096) per sequence, "
+                    "gen 512, block 32, block index U{0..15} and U{1..32} masked rows per sequence, DualCache, "
+                    "vocab 152064, calibrated confidences, tau 0.7; one step = 28 x block attention (one cache per layer) + 1 x threshold "
+                    "unmask with block advance + refresh of the finished sequences' 28 layer caches",
+               steps=50, warmup=10, layers=28, logit_sets=2),
     "c2": dict(desc="LLaDA-8B-shaped layer: batch 1, 32 heads x 128 (MHA), prompt 512 + gen 256, block 32, "
                     "DualCache, block index 0..7 swept, tau in {0.7, 0.9, 1.0}, vocab 126464; "
                     "one block-step = refresh + attention + unmask",
@@ -75,7 +95,13 @@ WORKLOADS = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
+    ap.add_argument("--sweep-block-size", action="store_true",
+                    help="large-batch LLaDA-8B layer: attention + unmask per call at block sizes 4..128")
+    ap.add_argument("--sweep-tau", action="store_true",
+                    help="large-batch LLaDA-8B layer: decode blocks at thresholds 0.5..1.0, tokens per step")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the all-core oracle baseline (0: the CPUs this process may use)")
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None, help="rotating cache/source sets")
@@ -97,7 +123,8 @@ def parse():
     args = ap.parse_args()
     w = WORKLOADS[args.workload]
     for key in ("steps", "warmup", "layers", "logit_sets"):
-        if getattr(args, key) is None and not ((args.lmhead or args.decode_block) and key in ("steps", "warmup")):
+        if getattr(args, key) is None and not ((args.lmhead or args.decode_block or args.sweep_block_size
+                                                 or args.sweep_tau) and key in ("steps", "warmup")):
             setattr(args, key, w[key])
     return args
 
@@ -646,6 +673,389 @@ def decode_block_main(args):
     print(json.dumps(result), flush=True)
 
 
+C5_LAYERS = 28
+C5_TAU = 0.7
+
+
+def cpu_threads(requested: int = 0) -> int:
+    """Threads for the all-core oracle baseline: the CPUs this process may
+    run on, capped by OMP_NUM_THREADS when the environment sets it."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return requested if requested > 0 else n
+
+
+def c5_cpu_baseline(s, inp, logits, tokens, mask, srcs, done, threads: int):
+    """The fp64 oracle on the host for the ragged Dream-7B step, BLAS limited
+    to `threads`: one layer's block attention over all 64 sequences, the
+    step's threshold unmask, and one layer's refresh of the finished
+    sequences, each timed once; the full step is 28 x attention + unmask +
+    28 x refresh, so the rate is 28 / that time (layer block-steps/s, the
+    unit of `value`)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attn_ref, refresh_ref, unmask_ref
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        attn_ref(inp.q, inp.k_new, inp.v_new, inp.k_cache, inp.v_cache, s.prompt_lens, s.gen_len, s.block_size,
+                 s.block_idxs, "dual")
+        t1 = time.perf_counter()
+        unmask_ref(logits, tokens, mask, s.prompt_lens, s.gen_len, s.block_size, s.block_idxs, C5_TAU,
+                   advance=True)
+        t2 = time.perf_counter()
+        if done:
+            refresh_ref(srcs[0], srcs[1], inp.k_cache, inp.v_cache, s.prompt_lens, s.gen_len, s.block_size,
+                        s.block_idxs, "dual", seq_ids=done)
+        t3 = time.perf_counter()
+    t_attn, t_unm, t_ref = t1 - t0, t2 - t1, t3 - t2
+    t_step = C5_LAYERS * (t_attn + t_ref) + t_unm
+    return {"value": round(C5_LAYERS / t_step, 4), "unit": "block-steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"one layer of the ragged Dream-7B step on the host (fp64 NumPy oracle, BLAS threads = "
+                      f"{threads}): attention of all 64 sequences {t_attn:.2f} s, threshold unmask of the batch "
+                      f"{t_unm:.2f} s, refresh of the {len(done)} finished sequences {t_ref:.2f} s; full step "
+                      f"= 28 x (attention + refresh) + unmask = {t_step:.1f} s",
+            "attn_s": round(t_attn, 3), "unmask_s": round(t_unm, 3), "refresh_s": round(t_ref, 3)}
+
+
+def c5_main(args):
+    """The ragged Dream-7B 28-layer step (the default workload)."""
+    import numpy as np
+    import torch
+
+    import block_wise_kv_amd as fd
+    from workloads import make_attn_inputs, make_decode_state, make_logits, make_refresh_src, n_masked_c5, shape_c5
+
+    def note(msg):
+        print(f"[bench c5] {msg}", file=sys.stderr, flush=True)
+
+    fd.lib()
+    dev = "cuda"
+    s = shape_c5()
+    b, Hq, Hkv, d, B, V, G, Lcap = (s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.block_size, s.vocab,
+                                    s.gen_len, s.max_seq_len)
+    nL = args.layers
+    K, W = args.steps, args.warmup
+    n_steps = W + K
+    bf = torch.bfloat16
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev).to(bf)
+
+    note(f"generating inputs: 64 sequences, L = {int(s.prompt_lens.min()) + G}..{int(s.prompt_lens.max()) + G}")
+    inp = make_attn_inputs(s, "dual")
+    srcs = make_refresh_src(s)
+    logits = make_logits(s, "calibrated")
+    n_masked = n_masked_c5(s)
+    tokens, mask = make_decode_state(s, n_masked)
+    # per layer: caches, refresh sources, fresh rows and output of its own
+    kc0, vc0, ks0, vs0 = up(inp.k_cache), up(inp.v_cache), up(srcs[0]), up(srcs[1])
+    q0, kn0, vn0 = up(inp.q), up(inp.k_new), up(inp.v_new)
+    kc = [kc0.clone() for _ in range(nL)]
+    vc = [vc0.clone() for _ in range(nL)]
+    ks = [ks0.clone() for _ in range(nL)]
+    vs = [vs0.clone() for _ in range(nL)]
+    qs = [q0.clone() for _ in range(nL)]
+    kns = [kn0.clone() for _ in range(nL)]
+    vns = [vn0.clone() for _ in range(nL)]
+    outs = [torch.empty_like(q0) for _ in range(nL)]
+    del kc0, vc0, ks0, vs0, q0, kn0, vn0
+    lg0 = up(logits)
+    lgs = [lg0.clone() for _ in range(args.logit_sets)]
+    del lg0
+    note(f"device inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+    # every step starts from the same state: its own tokens, mask and block indices
+    pl = torch.from_numpy(s.prompt_lens.astype(np.int32)).to(dev)
+    tok0 = torch.from_numpy(tokens).to(dev)
+    mask0 = torch.from_numpy(mask).to(dev)
+    bidx0 = torch.from_numpy(s.block_idxs.astype(np.int32)).to(dev)
+    tok = torch.stack([tok0] * n_steps)
+    msk = torch.stack([mask0] * n_steps)
+    bidx = torch.stack([bidx0] * n_steps)
+    maxP = int(s.prompt_lens.max())
+    seqs = [fd.seq_desc(b, Lcap, G, B, prompt_lens=pl, block_idxs=bidx[st], max_prompt_len=maxP)
+            for st in range(n_steps)]
+    nd = torch.zeros(b, dtype=torch.int32, device=dev)
+    dpos = torch.zeros((b, B), dtype=torch.int32, device=dev)
+    done = torch.zeros(b, dtype=torch.int32, device=dev)
+    n_done = torch.zeros(1, dtype=torch.int32, device=dev)
+    ad = fd.attn_desc(Hq, Hkv, d, fd.BF16)
+    ws_attn = fd.new_workspace(fd.block_attn_workspace(seqs[0], ad, "dual", B))
+    ws_unm = fd.new_workspace(fd.unmask_workspace(seqs[0], V, fd.BF16))
+
+    def reset_state():
+        tok.copy_(tok0.expand_as(tok))
+        msk.copy_(mask0.expand_as(msk))
+        bidx.copy_(bidx0.expand_as(bidx))
+
+    def step(st, events=None, names=None):
+        sq = seqs[st]
+        calls = []
+        for l in range(nL):
+            calls.append(("block_attn", lambda l=l: fd.block_attn(sq, "dual", qs[l], kns[l], vns[l], kc[l], vc[l],
+                                                                  outs[l], ws_attn)))
+        calls.append(("unmask_threshold", lambda: fd.unmask_threshold(
+            sq, lgs[st % len(lgs)], C5_TAU, tok[st], msk[st], nd, dpos, None, done, n_done, ws_unm,
+            flags=fd.UNMASK_ADVANCE_BLOCK)))
+        for l in range(nL):
+            calls.append(("kv_refresh", lambda l=l: fd.kv_refresh(sq, "dual", ks[l], vs[l], kc[l], vc[l], done,
+                                                                  n_done)))
+        for name, fn in calls:
+            if events is not None:
+                m = len(names)
+                fd.set_timing_events(events.ev[2 * m], events.ev[2 * m + 1])
+                names.append(name)
+            fn()
+
+    reset_state()
+    torch.cuda.synchronize()
+    note(f"capturing {W} warm-up and {K} timed steps ({2 * nL + 1} calls each) in HIP graphs")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        g_warm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_warm, stream=stream):
+            for st in range(W):
+                step(st)
+        g_timed = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_timed, stream=stream):
+            for st in range(W, n_steps):
+                step(st)
+    torch.cuda.synchronize()
+    g_warm.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g_timed.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    note(f"timed region: {K} steps in {elapsed * 1e3:.2f} ms")
+    # what the step decoded and which sequences it refreshed (every step
+    # starts from the same state, so every step's lists are the same)
+    n_dec_step = int(nd.sum().item())
+    done_list = sorted(int(x) for x in done.cpu().numpy()[:int(n_done.item())])
+
+    # the same K steps again, every call bracketed by its own events
+    reset_state()
+    torch.cuda.synchronize()
+    events = HipEvents(2 * K * (2 * nL + 1))
+    names = []
+    for st in range(W, n_steps):
+        step(st, events, names)
+    torch.cuda.synchronize()
+    L = s.prompt_lens.astype(np.int64) + G
+    attn_bytes = 2 * Hkv * d * 2 * int(L.sum()) + 2 * b * B * Hq * d * 2  # K/V rows once + Q read + out written
+    unm_bytes = int(n_masked.sum()) * V * 2
+    ref_bytes = sum(2 * 2 * int(L[i]) * Hkv * d * 2 for i in done_list)
+    per = {}
+    for m, name in enumerate(names):
+        e = per.setdefault(name, [])
+        e.append(events.elapsed_s(2 * m, 2 * m + 1))
+    events.close()
+    copy_bps = large_copy_rate()
+    flops_attn = 4 * b * Hq * B * int(L.sum()) * d
+    nbytes = {"block_attn": attn_bytes, "unmask_threshold": unm_bytes, "kv_refresh": ref_bytes}
+    kernels = {}
+    for name, ts in per.items():
+        avg = sum(ts) / len(ts)
+        gbs = nbytes[name] / avg / 1e9
+        kernels[name] = {"avg_us": round(avg * 1e6, 3), "launches": len(ts), "bytes": nbytes[name],
+                         "GB_per_s": round(gbs, 1), "frac_of_8TBps": round(gbs * 1e9 / PEAK_HBM_BPS, 4),
+                         "frac_of_copy": round(gbs * 1e9 / copy_bps, 4)}
+    kernels["block_attn"]["TFLOP_per_s"] = round(flops_attn / (sum(per["block_attn"]) / len(per["block_attn"]))
+                                                 / 1e12, 2)
+    total = {n: sum(ts) for n, ts in per.items()}
+    dom = max(total, key=total.get)
+    dk = kernels[dom]
+    t_au = (kernels["block_attn"]["avg_us"] + kernels["unmask_threshold"]["avg_us"]) * 1e-6
+    value = nL * K / elapsed
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "block-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS["c5"]["desc"], "name": "c5", "layers": nL,
+                   "block_steps_per_step": nL, "sum_seq_len": int(L.sum()), "masked_rows": int(n_masked.sum()),
+                   "logits": "calibrated", "tau": C5_TAU, "graph": True},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dk["GB_per_s"], 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(dk["GB_per_s"] / 8000.0, 4),
+                     "traffic": measured_traffic("c5", dom), "algorithmic_bytes": dk["bytes"]},
+        "kernels": kernels,
+        "large_copy_GB_per_s": round(copy_bps / 1e9, 1),
+        "model_steps_per_s": round(K / elapsed, 2),
+        "sequence_block_steps_per_s": round(value * b, 1),
+        "attn_unmask_block_steps_per_s": round(1.0 / t_au, 1),
+        "attn_unmask_sequence_block_steps_per_s": round(b / t_au, 1),
+        "step_telemetry": {"tokens_decoded": n_dec_step, "sequences_refreshed": len(done_list),
+                           "refresh_us_per_step": round(kernels["kv_refresh"]["avg_us"] * nL, 2),
+                           "refresh_us_per_layer_block_step": round(kernels["kv_refresh"]["avg_us"], 3)},
+    }
+    if not args.no_cpu_baseline:
+        note("timing the fp64 oracle on the host")
+        del kc, vc, ks, vs, lgs
+        n_all = cpu_threads(args.cpu_threads)
+        base = c5_cpu_baseline(s, inp, logits, tokens, mask, srcs, done_list, n_all)
+        one = c5_cpu_baseline(s, inp, logits, tokens, mask, srcs, done_list, 1) if n_all > 1 else base
+        base["one_thread"] = {"value": one["value"], "cores": 1, "sample": one["sample"]}
+        result["cpu_baseline"] = base
+    print(json.dumps(result), flush=True)
+
+
+SWEEP_BLOCKS = (4, 8, 16, 32, 64, 128)
+SWEEP_TAUS = (0.5, 0.6, 0.7, 0.8, 0.9, 1.0)
+
+
+def _c4_common(max_block):
+    """Caches, refresh-free attention inputs and peak logits of the
+    large-batch LLaDA-8B layer for block sizes up to `max_block`.  The
+    caches do not depend on the block size (same seeds); the logits of
+    block size B are the first B rows of the `max_block`-row draw."""
+    import numpy as np
+    import torch
+    from workloads import make_attn_inputs, make_logits, shape_c4
+    dev = "cuda"
+    bf = torch.bfloat16
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev).to(bf)
+    s_max = shape_c4(max_block, 0)
+    a = make_attn_inputs(s_max, "dual")
+    kc, vc = up(a.k_cache), up(a.v_cache)
+    del a
+    lg = up(make_logits(s_max, "peak"))
+    return kc, vc, lg
+
+
+def sweep_block_size_main(args):
+    """Attention + threshold unmask of the large-batch LLaDA-8B layer
+    (batch 32, 32 heads x 128, prompt 2048 + gen 512, DualCache) at each
+    block size: per-call HIP events over K calls each (eager)."""
+    import numpy as np
+    import torch
+
+    import block_wise_kv_amd as fd
+    from workloads import make_attn_inputs, make_decode_state, shape_c4
+    fd.lib()
+    dev = "cuda"
+    K = args.steps or 20
+    W = args.warmup if args.warmup is not None else 3
+    kc, vc, lg_all = _c4_common(max(SWEEP_BLOCKS))
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev).to(torch.bfloat16)
+    rows = []
+    ev = HipEvents(4 * (W + K))
+    for B in SWEEP_BLOCKS:
+        k = (512 // B) // 2
+        s = shape_c4(B, k)
+        a = make_attn_inputs(s, "dual", caches=False)
+        q, kn, vn = up(a.q), up(a.k_new), up(a.v_new)
+        out = torch.empty_like(q)
+        seq = fd.seq_desc(s.batch, s.max_seq_len, s.gen_len, B, 2048, k)
+        ad = fd.attn_desc(32, 32, 128, fd.BF16)
+        ws = fd.new_workspace(fd.block_attn_workspace(seq, ad, "dual", B))
+        lg = lg_all[:, :B]
+        tok0, msk0 = make_decode_state(s)
+        tok0, msk0 = torch.from_numpy(tok0).to(dev), torch.from_numpy(msk0).to(dev)
+        tk, mk = tok0.clone(), msk0.clone()
+        nd = torch.zeros(s.batch, dtype=torch.int32, device=dev)
+        uws = fd.new_workspace(fd.unmask_workspace(seq, s.vocab, fd.BF16))
+        torch.cuda.synchronize()
+        for r in range(W + K):
+            tk.copy_(tok0)
+            mk.copy_(msk0)
+            fd.set_timing_events(ev.ev[4 * r], ev.ev[4 * r + 1])
+            fd.block_attn(seq, "dual", q, kn, vn, kc, vc, out, ws)
+            fd.set_timing_events(ev.ev[4 * r + 2], ev.ev[4 * r + 3])
+            fd.unmask_threshold(seq, lg, 0.9, tk, mk, nd, workspace=uws)
+        torch.cuda.synchronize()
+        t_a = sum(ev.elapsed_s(4 * r, 4 * r + 1) for r in range(W, W + K)) / K
+        t_u = sum(ev.elapsed_s(4 * r + 2, 4 * r + 3) for r in range(W, W + K)) / K
+        L = 2048 + 512
+        ab = 2 * s.batch * 32 * L * 128 * 2 + 2 * s.batch * B * 32 * 128 * 2
+        ub = s.batch * B * s.vocab * 2
+        rows.append({"block_size": B, "block_idx": k, "attn_us": round(t_a * 1e6, 2), "unmask_us": round(t_u * 1e6, 2),
+                     "attn_bytes": ab, "unmask_bytes": ub,
+                     "attn_frac_of_8TBps": round(ab / t_a / PEAK_HBM_BPS, 4),
+                     "unmask_frac_of_8TBps": round(ub / t_u / PEAK_HBM_BPS, 4),
+                     "attn_TFLOP_per_s": round(4 * s.batch * 32 * B * L * 128 / t_a / 1e12, 1),
+                     "block_steps_per_s": round(1.0 / (t_a + t_u), 1),
+                     "sequence_block_steps_per_s": round(s.batch / (t_a + t_u), 1)})
+        print(f"[sweep] B={B}: attention {t_a * 1e6:.1f} us, unmask {t_u * 1e6:.1f} us", file=sys.stderr, flush=True)
+        del q, kn, vn, out, ws, uws
+    ev.close()
+    print(json.dumps({"metric": "block-steps/s per layer (attn+unmask) and HBM fraction across block sizes, 1 GPU",
+                      "config": {"workload": WORKLOADS["c4"]["desc"].replace("block 32", "block size swept"),
+                                 "name": "c4_block_size_sweep", "tau": 0.9, "logits": "peak", "calls": K},
+                      "sweep": rows}), flush=True)
+
+
+def sweep_tau_main(args):
+    """Decode the large-batch LLaDA-8B layer's current block (batch 32,
+    block 32, every block row masked at the first step) at each threshold:
+    per step, the block attention and one threshold unmask whose logits come
+    from a fresh seeded draw of the calibrated recipe (confidence u ~ U(0.5,
+    1) per row; four draws rotate over the steps), until every sequence's
+    block is done; records the tokens decoded per step and times each
+    step's two calls with HIP events."""
+    import numpy as np
+    import torch
+
+    import block_wise_kv_amd as fd
+    from workloads import make_attn_inputs, make_decode_state, make_logits, shape_c4
+    fd.lib()
+    dev = "cuda"
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev).to(torch.bfloat16)
+    s = shape_c4(32, 8)
+    a = make_attn_inputs(s, "dual")
+    q, kn, vn, kc, vc = (up(x) for x in (a.q, a.k_new, a.v_new, a.k_cache, a.v_cache))
+    del a
+    out = torch.empty_like(q)
+    lgs = [up(make_logits(s, "calibrated", step=st)) for st in range(4)]
+    seq = fd.seq_desc(s.batch, s.max_seq_len, s.gen_len, 32, 2048, 8)
+    ad = fd.attn_desc(32, 32, 128, fd.BF16)
+    ws = fd.new_workspace(fd.block_attn_workspace(seq, ad, "dual", 32))
+    uws = fd.new_workspace(fd.unmask_workspace(seq, s.vocab, fd.BF16))
+    tok0, msk0 = make_decode_state(s)
+    tok0, msk0 = torch.from_numpy(tok0).to(dev), torch.from_numpy(msk0).to(dev)
+    nd = torch.zeros(s.batch, dtype=torch.int32, device=dev)
+    done = torch.zeros(s.batch, dtype=torch.int32, device=dev)
+    n_done = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev = HipEvents(4 * 32)
+    rows = []
+    for tau in SWEEP_TAUS:
+        tk, mk = tok0.clone(), msk0.clone()
+        per_step = []
+        t_a = t_u = 0.0
+        for st in range(32):
+            fd.set_timing_events(ev.ev[4 * st], ev.ev[4 * st + 1])
+            fd.block_attn(seq, "dual", q, kn, vn, kc, vc, out, ws)
+            fd.set_timing_events(ev.ev[4 * st + 2], ev.ev[4 * st + 3])
+            fd.unmask_threshold(seq, lgs[st % 4], tau, tk, mk, nd, None, None, done, n_done, uws)
+            torch.cuda.synchronize()
+            t_a += ev.elapsed_s(4 * st, 4 * st + 1)
+            t_u += ev.elapsed_s(4 * st + 2, 4 * st + 3)
+            per_step.append(int(nd.sum().item()))
+            if int(n_done.item()) == s.batch:
+                break
+        n = len(per_step)
+        rows.append({"tau": tau, "steps_to_finish_block": n, "tokens_per_step": per_step,
+                     "mean_tokens_per_step_per_sequence": round(sum(per_step) / n / s.batch, 3),
+                     "attn_us_per_step": round(t_a / n * 1e6, 2), "unmask_us_per_step": round(t_u / n * 1e6, 2),
+                     "layer_us_per_block": round((t_a + t_u) * 1e6, 1)})
+        print(f"[sweep] tau={tau}: {n} steps, {sum(per_step)} tokens", file=sys.stderr, flush=True)
+    ev.close()
+    print(json.dumps({"metric": "tokens decoded per step and steps per block across thresholds, 1 GPU",
+                      "config": {"workload": "Large-batch LLaDA-8B-shaped layer: batch 32, 32 heads x 128, prompt "
+                                             "2048 + gen 512, block 32 (block index 8), DualCache, calibrated "
+                                             "confidences u ~ U(0.5, 1), four logits draws rotating over the steps",
+                                 "name": "c4_tau_sweep"},
+                      "sweep": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -660,6 +1070,15 @@ def main():
         return
     if args.decode_block:
         decode_block_main(args)
+        return
+    if args.sweep_block_size:
+        sweep_block_size_main(args)
+        return
+    if args.sweep_tau:
+        sweep_tau_main(args)
+        return
+    if args.workload == "c5":
+        c5_main(args)
         return
     import torch
 

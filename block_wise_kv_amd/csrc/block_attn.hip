@@ -42,8 +42,8 @@
 // the same XCD (workgroups are dealt round-robin over the 8 XCDs): they
 // then read the same K/V rows through one L2.
 //
-// f32 (any mode, d = 64 or 128): a plain VALU kernel, one wave per query
-// row, fp32 throughout.
+// f32 (any mode, d = 64 or 128) and bf16 with d = 64: a plain vector-ALU
+// kernel, one wave per query row, fp32 arithmetic.
 #include <float.h>
 #include <stdlib.h>
 
@@ -1353,9 +1353,23 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ f32 VALU
-template <int D>
-__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
+// ------------------------------------------------------------------ vector ALU
+// fp32 inputs (d = 64 or 128) and bf16 inputs with d = 64: one wave per
+// query row, every product and sum in fp32; the lanes take 64 keys at a
+// time for the scores, then every lane accumulates its head-dim columns of
+// P V over those keys.  The output is stored in the input dtype.
+__device__ __forceinline__ float4 load4(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 w = *(const uint2*)p;
+  return make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
+}
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+__device__ __forceinline__ float load1(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+__device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store1(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_bits(v); }
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   constexpr int U = D / 64;
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + wid;
@@ -1371,17 +1385,16 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   __shared__ float s_q[4][D];
   if (r >= g.nq) return;
 
-  const float* qrow = (const float*)a.q + (((size_t)g.i * a.fresh_rows + r) * a.Hq + h) * D;
+  const T* qrow = (const T*)a.q + (((size_t)g.i * a.fresh_rows + r) * a.Hq + h) * D;
 #pragma unroll
-  for (int u = 0; u < U; ++u) s_q[wid][lane + 64 * u] = qrow[lane + 64 * u];
+  for (int u = 0; u < U; ++u) s_q[wid][lane + 64 * u] = load1(qrow + lane + 64 * u);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  const float* kn = (const float*)a.kn;
-  const float* vn = (const float*)a.vn;
-  const float* kc = (const float*)a.kc;
-  const float* vc = (const float*)a.vc;
+  const T* kn = (const T*)a.kn;
+  const T* vn = (const T*)a.vn;
+  const T* kc = (const T*)a.kc;
+  const T* vc = (const T*)a.vc;
   float acc[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) acc[u] = 0.f;
@@ -1390,11 +1403,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const int j = j0 + lane;
     float s = -INFINITY;
     if (j < g.L) {
-      const float4* krow = (const float4*)kv_row(a, kn, kc, g, j, D);
+      const T* krow = kv_row(a, kn, kc, g, j, D);
       float dot = 0.f;
 #pragma unroll 8
       for (int d4 = 0; d4 < D / 4; ++d4) {
-        const float4 kv = krow[d4];
+        const float4 kv = load4(krow + 4 * d4);
         dot = fmaf(s_q[wid][4 * d4 + 0], kv.x, dot);
         dot = fmaf(s_q[wid][4 * d4 + 1], kv.y, dot);
         dot = fmaf(s_q[wid][4 * d4 + 2], kv.z, dot);
@@ -1412,15 +1425,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const int nk = min(64, g.L - j0);
     for (int jj = 0; jj < nk; ++jj) {
       const float pj = __shfl(p, jj, 64);
-      const float* vrow = kv_row(a, vn, vc, g, j0 + jj, D);
+      const T* vrow = kv_row(a, vn, vc, g, j0 + jj, D);
 #pragma unroll
-      for (int u = 0; u < U; ++u) acc[u] = fmaf(pj, vrow[lane + 64 * u], acc[u]);
+      for (int u = 0; u < U; ++u) acc[u] = fmaf(pj, load1(vrow + lane + 64 * u), acc[u]);
     }
   }
-  float* orow = (float*)a.out + (((size_t)g.i * a.fresh_rows + r) * a.Hq + h) * D;
+  T* orow = (T*)a.out + (((size_t)g.i * a.fresh_rows + r) * a.Hq + h) * D;
   const float inv = 1.f / l;
 #pragma unroll
-  for (int u = 0; u < U; ++u) orow[lane + 64 * u] = acc[u] * inv;
+  for (int u = 0; u < U; ++u) store1(orow + lane + 64 * u, acc[u] * inv);
 }
 
 // ------------------------------------------------------------------ planning
@@ -1430,10 +1443,17 @@ static long env_long(const char* name, long dflt) {
   return v > 0 ? v : dflt;
 }
 
-static int g_attn_qt = 0, g_attn_wgs = 0;  // fdllm_set_tuning overrides (0: automatic)
+// fdllm_set_tuning overrides (0: automatic), per host thread: a workspace
+// query and the call it sizes see the same plan when made on one thread.
+static thread_local int g_attn_qt = 0, g_attn_wgs = 0;
 void set_attn_tuning(int qt, int wgs) {
   g_attn_qt = qt;
   g_attn_wgs = wgs;
+}
+
+static long attn_env_target() {
+  static const long v = env_long("FDLLM_ATTN_TARGET_WGS", 0);
+  return v;
 }
 
 // Kernel and work split (see the choice of QT below).  The key split fills
@@ -1442,9 +1462,8 @@ void set_attn_tuning(int qt, int wgs) {
 // with 8 waves of one query tile each) and FDLLM_ATTN_TARGET_WGS override
 // the defaults for tuning.
 AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max) {
-  (void)d;
   AttnPlan p{};
-  if (dtype != 0) {
+  if (dtype != 0 || d != kD) {  // vector-ALU kernel: four query rows per workgroup
     p.n_qt = (nq_max + 3) / 4;
     p.n_grp = 1;
     p.n_split = 1;
@@ -1467,7 +1486,6 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   // tile.
   if (QT != 1 && QT != 2 && QT != 4 && QT != 8) QT = p.n_qt == 1 ? (g >= 4 ? 8 : 1) : (T >= 4 ? 4 : 2);
   p.qt_per_wg = QT;
-  static const long target_env = env_long("FDLLM_ATTN_TARGET_WGS", 0);
   long base;
   int unit;
   if (QT == 1) {  // split-key kernel: one item per (sequence, query head, query tile, key chunk)
@@ -1483,6 +1501,7 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
     base = (long)b * Hkv * p.n_grp;
     unit = kKT * (4 / QT);  // keys per ring round
   }
+  const long target_env = attn_env_target();
   const long target = g_attn_wgs > 0 ? g_attn_wgs : target_env > 0 ? target_env : (QT == 4 ? 512 : 256);
   const int max_split = (L_max + unit - 1) / unit;
   int ns = (int)((target + base / 2) / base);  // nearest: one chunk unless the items fall well short
@@ -1501,31 +1520,60 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
     const size_t slots = (size_t)b * Hq * p.n_qt * ns;
     const size_t slot_bytes = (QT == 8 || QT == 1) ? (size_t)kPart16Bytes : kPartFloats * sizeof(float);
     p.part_bytes = ((slots * slot_bytes) + 255) & ~(size_t)255;
-    // arrival counters for the in-kernel merge (the 8-tile ring is merged by
-    // a second kernel and needs none)
-    const size_t counters = QT == 1 ? (size_t)b * Hq * p.n_qt : QT == 8 ? 0 : (size_t)base;
-    const size_t bytes = p.part_bytes + counters * sizeof(uint32_t);
-    p.ws_bytes = (bytes + 255) & ~(size_t)255;
   }
   return p;
 }
 
-void attn_bind_workspace(AttnArgs& a, const AttnPlan& p, void* workspace) {
+// Workspace layout: the arrival counters of the in-kernel merges first, one
+// per (sequence, query head, query tile) of the largest query-row count the
+// geometry allows (nq_bound: the block size with DualCache, the generation
+// length with the prefix cache, prompt + generation without a cache), then
+// the split partials.  The counters therefore sit at the same place, and
+// only ever hold zeros between calls, whatever the block index, the
+// per-call row count or the kernel the planner picks: one workspace zeroed
+// once serves every block index of a geometry.  Each kernel's counter index
+// is below b * Hq * n_qt (the 4-wave ring's groups, b * Hkv * n_grp, are
+// fewer; the 8-wave ring uses none).
+size_t attn_counter_bytes(int b, int Hq, int nq_bound) {
+  const size_t n = (size_t)b * Hq * ((nq_bound + kQT - 1) / kQT);
+  return (n * sizeof(uint32_t) + 255) & ~(size_t)255;
+}
+
+// Bytes of a workspace that serves every call of the geometry: the counters
+// and the largest partial area over every query-row count up to nq_bound.
+// A plan has one key chunk (no partials) once its work items reach the
+// workgroup target, and every kernel's item count is at least
+// b * Hq * n_qt / 8, so the scan stops there.
+size_t attn_workspace_bytes(int dtype, int b, int Hq, int Hkv, int d, int nq_bound, int L_max) {
+  if (dtype != 0 || d != kD) return 0;
+  const long target_env = attn_env_target();
+  const long tmax = g_attn_wgs > 0 ? g_attn_wgs : target_env > 0 ? target_env : 512;
+  const int nqt_bound = (nq_bound + kQT - 1) / kQT;
+  size_t part = 0;
+  for (int t = 1; t <= nqt_bound; ++t) {
+    const AttnPlan p = plan_block_attn(dtype, b, Hq, Hkv, d, t < nqt_bound ? t * kQT : nq_bound, L_max);
+    if (p.part_bytes > part) part = p.part_bytes;
+    if ((long)b * Hq * t >= 8 * tmax) break;
+  }
+  return part > 0 ? attn_counter_bytes(b, Hq, nq_bound) + part : 0;
+}
+
+void attn_bind_workspace(AttnArgs& a, const AttnPlan& p, void* workspace, size_t counter_bytes) {
   a.n_qt = p.n_qt;
   a.n_grp = p.n_grp;
   a.n_split = p.n_split;
   a.kchunk = p.kchunk;
   a.n_items = p.n_items;
   a.per_xcd = p.per_xcd;
-  if (p.ws_bytes > 0) {
-    a.part = (float*)workspace;
-    a.cnt = (uint32_t*)((char*)workspace + p.part_bytes);
+  if (p.part_bytes > 0) {
+    a.cnt = (uint32_t*)workspace;
+    a.part = (float*)((char*)workspace + counter_bytes);
   }
 }
 
 hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, int d, hipStream_t st) {
   const LaunchEvents ev = take_launch_events();
-  if (dtype == 0) {
+  if (dtype == 0 && d == kD) {
     const dim3 grid((unsigned)p.grid), block(kThreads);
     if (p.qt_per_wg == 8) {
       auto* kern = attn_gqa_kernel<4>;
@@ -1541,8 +1589,9 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, in
     return launch_kernel(attn_split_kernel, grid, block, 0, st, ev.start, ev.stop, a);
   }
   dim3 grid((unsigned)p.n_qt, (unsigned)a.Hq, (unsigned)a.sq.b);
-  return d == 64 ? launch_kernel(attn_f32_kernel<64>, grid, dim3(256), 0, st, ev.start, ev.stop, a)
-                 : launch_kernel(attn_f32_kernel<128>, grid, dim3(256), 0, st, ev.start, ev.stop, a);
+  if (dtype == 0) return launch_kernel(attn_valu_kernel<uint16_t, 64>, grid, dim3(256), 0, st, ev.start, ev.stop, a);
+  return d == 64 ? launch_kernel(attn_valu_kernel<float, 64>, grid, dim3(256), 0, st, ev.start, ev.stop, a)
+                 : launch_kernel(attn_valu_kernel<float, 128>, grid, dim3(256), 0, st, ev.start, ev.stop, a);
 }
 
 }  // namespace fdllm

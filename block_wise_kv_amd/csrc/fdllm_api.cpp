@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "fdllm.h"
@@ -39,14 +40,17 @@ fdllm_status ok() {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Debug checks of device-resident arrays: FDLLM_DEBUG=1 in the environment
-// (read once) or fdllm_set_debug.
-int g_debug = -1;
+// (read once) or fdllm_set_debug (process-wide, read atomically).
+std::atomic<int> g_debug{-1};
 bool debug_on() {
-  if (g_debug < 0) {
+  int v = g_debug.load(std::memory_order_relaxed);
+  if (v < 0) {
     const char* e = getenv("FDLLM_DEBUG");
-    g_debug = (e && atoi(e) != 0) ? 1 : 0;
+    int expected = -1;
+    g_debug.compare_exchange_strong(expected, (e && atoi(e) != 0) ? 1 : 0, std::memory_order_relaxed);
+    v = g_debug.load(std::memory_order_relaxed);
   }
-  return g_debug == 1;
+  return v == 1;
 }
 
 // In debug mode, validate the device arrays a call is about to use (a
@@ -135,9 +139,13 @@ int fresh_len_uniform(int mode, int P, int G, int B, int k) {
 struct AttnSetup {
   SeqArgs sa;
   int max_P;
-  int nq_max;
+  int nq_max;               // query rows of this call (the bound when ragged)
+  int nq_bound;             // query rows of the geometry at any block index
   int L_max;
   AttnPlan plan;
+  size_t counter_bytes;     // counter region at the start of the workspace
+  size_t ws_call;           // bytes this call uses (0: no workspace)
+  size_t ws_geometry;       // bytes that serve every block index (the query's answer)
 };
 
 fdllm_status setup_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* ad, int32_t mode, int32_t fresh_rows,
@@ -148,10 +156,8 @@ fdllm_status setup_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* ad, in
   if (st) return st;
   if (mode < FDLLM_CACHE_NONE || mode > FDLLM_CACHE_DUAL)
     return fail(FDLLM_ERR_INVALID_ARG, "mode %d is not a fdllm_cache_mode", mode);
-  if (ad->dtype == FDLLM_BF16 && ad->head_dim != 128)
-    return fail(FDLLM_ERR_UNSUPPORTED, "bf16 attention supports head_dim 128 (got %d)", ad->head_dim);
-  if (ad->dtype == FDLLM_F32 && ad->head_dim != 64 && ad->head_dim != 128)
-    return fail(FDLLM_ERR_UNSUPPORTED, "f32 attention supports head_dim 64 or 128 (got %d)", ad->head_dim);
+  if (ad->head_dim != 64 && ad->head_dim != 128)
+    return fail(FDLLM_ERR_UNSUPPORTED, "attention supports head_dim 64 or 128 (got %d)", ad->head_dim);
   const bool ragged = seq->prompt_lens || seq->block_idxs;
   int need;
   if (!ragged) {
@@ -163,6 +169,8 @@ fdllm_status setup_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* ad, in
   if (fresh_rows < need)
     return fail(FDLLM_ERR_INVALID_ARG, "fresh_rows %d < %d rows needed by this mode/geometry", fresh_rows, need);
   su.nq_max = need;
+  su.nq_bound = mode == FDLLM_CACHE_DUAL ? seq->block_size
+              : mode == FDLLM_CACHE_PREFIX ? seq->gen_len : su.max_P + seq->gen_len;
   su.L_max = su.max_P + seq->gen_len;
   const int64_t q_elems = (int64_t)seq->batch * fresh_rows * ad->n_q_heads * ad->head_dim;
   const int64_t c_elems = (int64_t)seq->batch * ad->n_kv_heads * seq->max_seq_len * ad->head_dim;
@@ -171,6 +179,10 @@ fdllm_status setup_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* ad, in
   if ((int64_t)seq->batch * ad->n_q_heads * ((need + 31) / 32) * ((su.L_max + 127) / 128) >= ((int64_t)1 << 31))
     return fail(FDLLM_ERR_INVALID_ARG, "grid too large");
   su.plan = plan_block_attn(ad->dtype, seq->batch, ad->n_q_heads, ad->n_kv_heads, ad->head_dim, need, su.L_max);
+  su.counter_bytes = attn_counter_bytes(seq->batch, ad->n_q_heads, su.nq_bound);
+  su.ws_call = su.plan.part_bytes > 0 ? su.counter_bytes + su.plan.part_bytes : 0;
+  su.ws_geometry = attn_workspace_bytes(ad->dtype, seq->batch, ad->n_q_heads, ad->n_kv_heads, ad->head_dim,
+                                        su.nq_bound, su.L_max);
   return FDLLM_OK;
 }
 
@@ -314,7 +326,8 @@ extern "C" {
 fdllm_status fdllm_set_tuning(int32_t attn_qt, int32_t attn_wgs, int32_t unmask_wgs) {
   if (attn_qt != 0 && attn_qt != 1 && attn_qt != 2 && attn_qt != 4 && attn_qt != 8)
     return fail(FDLLM_ERR_INVALID_ARG, "attn_qt must be 0, 1, 2, 4 or 8 (got %d)", attn_qt);
-  if (attn_wgs < 0 || unmask_wgs < 0) return fail(FDLLM_ERR_INVALID_ARG, "workgroup targets must be >= 0");
+  if (attn_wgs < 0 || unmask_wgs < 0 || attn_wgs > 65536 || unmask_wgs > 65536)
+    return fail(FDLLM_ERR_INVALID_ARG, "workgroup targets must be in [0, 65536]");
   set_attn_tuning(attn_qt, attn_wgs);
   set_unmask_tuning(unmask_wgs);
   return ok();
@@ -322,7 +335,7 @@ fdllm_status fdllm_set_tuning(int32_t attn_qt, int32_t attn_wgs, int32_t unmask_
 
 fdllm_status fdllm_set_debug(int32_t on) {
   if (on != 0 && on != 1) return fail(FDLLM_ERR_INVALID_ARG, "on must be 0 or 1 (got %d)", on);
-  g_debug = on;
+  g_debug.store(on, std::memory_order_relaxed);
   return ok();
 }
 
@@ -336,7 +349,7 @@ size_t fdllm_block_attn_workspace(const fdllm_seq_desc* seq, const fdllm_attn_de
                                   int32_t fresh_rows) {
   AttnSetup su;
   if (setup_attn(seq, attn, mode, fresh_rows, su)) return 0;
-  return su.plan.ws_bytes;
+  return su.ws_geometry;
 }
 
 fdllm_status fdllm_block_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode,
@@ -359,9 +372,9 @@ fdllm_status fdllm_block_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
   if (ranges_overlap(out, qb, q, qb) || ranges_overlap(out, qb, k_new, kvb) || ranges_overlap(out, qb, v_new, kvb) ||
       (mode != FDLLM_CACHE_NONE && (ranges_overlap(out, qb, k_cache, cb) || ranges_overlap(out, qb, v_cache, cb))))
     return fail(FDLLM_ERR_INVALID_ARG, "out must not alias an input");
-  if (su.plan.ws_bytes > 0) {
-    if (!workspace || workspace_bytes < su.plan.ws_bytes)
-      return fail(FDLLM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", su.plan.ws_bytes,
+  if (su.ws_call > 0) {
+    if (!workspace || workspace_bytes < su.ws_call)
+      return fail(FDLLM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", su.ws_call,
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(FDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   }
@@ -382,7 +395,7 @@ fdllm_status fdllm_block_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
   a.kc = k_cache;
   a.vc = v_cache;
   a.out = out;
-  attn_bind_workspace(a, su.plan, workspace);
+  attn_bind_workspace(a, su.plan, workspace, su.counter_bytes);
   hipError_t e = launch_block_attn(a, su.plan, attn->dtype, attn->head_dim, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "block_attn launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -146,7 +146,7 @@ struct AttnArgs {
   const void* vc;
   void* out;
   float* part;              // split-key partials [b][Hq][n_qt][n_split] (null when n_split == 1)
-  uint32_t* cnt;            // split-key counters [b][Hkv][n_grp]
+  uint32_t* cnt;            // arrival counters of the in-kernel merges (start of the workspace)
   int n_qt;                 // query tiles per (sequence, query head)
   int n_grp;                // query-tile groups per (sequence, KV head)
   int n_split;              // key chunks per group
@@ -158,12 +158,13 @@ struct AttnArgs {
 struct AttnPlan {
   int qt_per_wg;            // query tiles sharing each K/V tile in a workgroup (1, 2 or 4)
   int n_qt, n_grp, n_split, kchunk, n_items, per_xcd, grid;
-  size_t part_bytes;        // split partials at the start of the workspace
-  size_t ws_bytes;
+  size_t part_bytes;        // split partials (after the counters); 0: one key chunk, no workspace
 };
 AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max);
 void set_attn_tuning(int qt, int wgs);
-void attn_bind_workspace(AttnArgs& a, const AttnPlan& p, void* workspace);
+size_t attn_counter_bytes(int b, int Hq, int nq_bound);
+size_t attn_workspace_bytes(int dtype, int b, int Hq, int Hkv, int d, int nq_bound, int L_max);
+void attn_bind_workspace(AttnArgs& a, const AttnPlan& p, void* workspace, size_t counter_bytes);
 hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, int d, hipStream_t st);
 
 // ------------------------------------------------------------------ misc

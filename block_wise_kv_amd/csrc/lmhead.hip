@@ -317,7 +317,7 @@ hipError_t launch_lmhead_pack(const void* w, void* wp, int V, int H, hipStream_t
 
 // Vocabulary tiles per wave: the environment variable FDLLM_LMHEAD_VT or
 // fdllm_set_lmhead_tuning (1 or 2) overrides the default.
-static int g_lmhead_vt = 0;
+static thread_local int g_lmhead_vt = 0;  // per host thread, like the other tuning overrides
 void set_lmhead_tuning(int vt) { g_lmhead_vt = vt; }
 static int lmhead_env_vt() {
   static int v = [] {

@@ -818,7 +818,7 @@ static long unmask_target_workgroups() {
   return v;
 }
 
-static int g_unmask_wgs = 0;  // fdllm_set_tuning override (0: automatic)
+static thread_local int g_unmask_wgs = 0;  // fdllm_set_tuning override (0: automatic), per host thread
 void set_unmask_tuning(int wgs) { g_unmask_wgs = wgs; }
 
 UnmaskPlan plan_unmask(int dtype, int V, int rows) {
@@ -840,26 +840,27 @@ UnmaskPlan plan_unmask(int dtype, int V, int rows) {
   return p;
 }
 
-// Workspace: chunk partials, the 16-byte finished-sequence counter, then
-// per-sequence done flags and arrival counters.  Zeroed once; every counter
-// is reset by its last user.
-size_t unmask_workspace_bytes(int b, int B, int nchunk) {
-  size_t bytes = (size_t)b * B * nchunk * sizeof(UnmaskPartial);  // chunk partials
-  bytes += 16;                                                    // global counter
-  bytes += (size_t)b * 8;                                         // done flags
-  bytes += (size_t)b * 4;                                         // sequence counters
+// Workspace: the 16-byte finished-sequence counter, the per-sequence done
+// flags and arrival counters first (their place depends only on the batch),
+// then the chunk partials.  Zeroed once; every counter is reset by its last
+// user, so the unmask calls and the fused LM-head calls of one batch can
+// share a workspace whatever their vocabulary split.
+static size_t unmask_counter_bytes(int b) {
+  const size_t bytes = 16 + (size_t)b * 8 + (size_t)b * 4;  // global counter, done flags, sequence counters
   return (bytes + 255) & ~(size_t)255;
+}
+
+size_t unmask_workspace_bytes(int b, int B, int nchunk) {
+  const size_t part = (size_t)b * B * nchunk * sizeof(UnmaskPartial);  // chunk partials
+  return unmask_counter_bytes(b) + ((part + 255) & ~(size_t)255);
 }
 
 void unmask_bind_workspace(UnmaskArgs& a, void* workspace) {
   char* w = (char*)workspace;
-  a.part = (UnmaskPartial*)w;
-  w += (size_t)a.sq.b * a.sq.B * a.nchunk * sizeof(UnmaskPartial);
   a.glob = (uint64_t*)w;
-  w += 16;
-  a.done_flag = (int32_t*)w;
-  w += (size_t)a.sq.b * 8;
-  a.seq_cnt = (uint32_t*)w;
+  a.done_flag = (int32_t*)(w + 16);
+  a.seq_cnt = (uint32_t*)(w + 16 + (size_t)a.sq.b * 8);
+  a.part = (UnmaskPartial*)(w + unmask_counter_bytes(a.sq.b));
 }
 
 hipError_t launch_unmask(const UnmaskArgs& a, int dtype, hipStream_t st) {

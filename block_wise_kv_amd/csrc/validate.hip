@@ -4,6 +4,8 @@
 // trusted.
 #include <limits.h>
 
+#include <mutex>
+
 #include "fdllm_device.h"
 #include "fdllm_internal.h"
 
@@ -11,9 +13,11 @@ namespace fdllm {
 
 // The first problem found: (sequence or list index) * 8 + code, minimised
 // over threads (INT_MAX: none).  A module-scope word, so the check needs no
-// allocation; debug calls on one device are therefore serialised by the
-// host synchronisation that reads it.
+// allocation; a host mutex held from its reset to the synchronisation that
+// reads it back makes concurrent debug-mode calls from several host threads
+// take turns.
 __device__ int g_validate_key;
+static std::mutex g_validate_mu;
 
 __global__ __launch_bounds__(256) void validate_kernel(SeqArgs sq, int max_P, const int32_t* seq_ids,
                                                       const int32_t* n_seq) {
@@ -43,6 +47,7 @@ __global__ __launch_bounds__(256) void validate_kernel(SeqArgs sq, int max_P, co
 
 hipError_t run_validate(const SeqArgs& sq, int max_P, const int32_t* seq_ids, const int32_t* n_seq, hipStream_t st,
                         int* key_out) {
+  std::lock_guard<std::mutex> lock(g_validate_mu);
   const int none = INT_MAX;
   hipError_t e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_validate_key), &none, sizeof(int), 0, hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return e;

@@ -26,12 +26,21 @@
  *     debug mode (fdllm_set_debug, or FDLLM_DEBUG=1 in the environment):
  *     then a validation kernel checks them and the call synchronises the
  *     stream to read its verdict before launching anything else.
- *   - No exception or abort crosses the ABI.  Thread-safe: no global
- *     device state; fdllm_last_error() is per host thread.
+ *   - No exception or abort crosses the ABI.  Thread-safe: calls keep no
+ *     state between them except per-host-thread settings (the last error,
+ *     the timing hook, the planner overrides) and the debug-mode switch;
+ *     debug-mode calls from several threads take turns on a host lock.
  *   - Workspaces hold self-resetting counters: zero a workspace once with
  *     fdllm_workspace_init after allocating it; every call leaves its
- *     counters at zero again.  Two calls that share a workspace must not
- *     run concurrently (same stream, or ordered streams).
+ *     counters at zero again.  The counters sit at the start of the
+ *     workspace, at a place fixed by the geometry (batch, heads, mode and
+ *     the row bounds below), never by the block index or the planner's
+ *     choice, so one workspace serves every block index of a decode loop.
+ *     A workspace belongs to one geometry at a time: a call of another
+ *     geometry may overwrite the counter area of the first with partial
+ *     results, so re-zero it when switching.  Two calls that share a
+ *     workspace must not run concurrently (same stream, or ordered
+ *     streams).
  *
  * Notation: batch b; sequence i has prompt length P_i, shared gen length G,
  * L_i = P_i + G; block size B (G % B == 0); block index k_i in [0, G/B);
@@ -89,7 +98,8 @@ typedef struct {
 typedef struct {
   int32_t n_q_heads;   /* Hq >= 1 */
   int32_t n_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0 */
-  int32_t head_dim;    /* d: 128 for bf16; 64 or 128 for f32 */
+  int32_t head_dim;    /* d: 64 or 128 (bf16 d = 128 runs on the matrix cores,
+                          bf16 d = 64 and f32 on the vector ALUs) */
   int32_t dtype;       /* fdllm_dtype of q, k, v, caches and out */
   float scale;         /* softmax scale; 0 selects 1/sqrt(d) */
 } fdllm_attn_desc;
@@ -98,8 +108,12 @@ typedef struct {
 /* (a) block attention                                                 */
 /* ------------------------------------------------------------------ */
 
-/* Bytes of workspace fdllm_block_attn needs for this geometry (0 when the
- * key range is not split across workgroups).  Returns 0 on invalid input. */
+/* Bytes of workspace fdllm_block_attn needs for this geometry at any block
+ * index (0 when no block index splits the key range across workgroups):
+ * the result does not depend on seq->block_idx or on fresh_rows beyond
+ * their validation, so it can be queried once for a whole decode loop.
+ * Calls check the bytes they use against workspace_bytes
+ * (FDLLM_ERR_WORKSPACE when short).  Returns 0 on invalid input. */
 size_t fdllm_block_attn_workspace(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn,
                                   int32_t mode, int32_t fresh_rows);
 
@@ -132,6 +146,9 @@ fdllm_status fdllm_block_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
 #define FDLLM_UNMASK_ADVANCE_BLOCK 1u /* k_i += 1 when block i is done and k_i + 1 < G/B
                                          (needs seq->block_idxs != NULL) */
 
+/* Workspace bytes of fdllm_unmask_threshold / _topk (0 on invalid input).
+ * Its counters (at the start, placed by the batch size alone) are shared
+ * with the fused LM-head calls of the same batch. */
 size_t fdllm_unmask_workspace(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype);
 
 /* One decoding step of the threshold rule ([README] item 2, [NEWS] item 2,
@@ -283,7 +300,8 @@ fdllm_status fdllm_workspace_init(void* workspace, size_t bytes, void* stream);
  * block_size, 0 <= *n_seq <= batch, 0 <= seq_ids[j] < batch for j < *n_seq
  * -- then synchronises `stream` and returns FDLLM_ERR_INVALID_ARG (naming
  * the first bad entry) without launching anything when one fails.  Not for
- * use under stream capture; debug calls on one device must not overlap.
+ * use under stream capture; concurrent debug-mode calls from several host
+ * threads take turns (a host lock spans each check).
  * 0 = the arrays are trusted (default).  FDLLM_ERR_INVALID_ARG for other
  * values. */
 fdllm_status fdllm_set_debug(int32_t on);
@@ -299,25 +317,28 @@ fdllm_status fdllm_set_timing_events(void* start_event, void* stop_event);
 /* Launch-planner overrides, for tuning and for tests that exercise every
  * kernel variant on one input.  0 keeps the automatic choice (which the
  * environment variables FDLLM_ATTN_QT, FDLLM_ATTN_TARGET_WGS and
- * FDLLM_UNMASK_TARGET_WGS also override).
+ * FDLLM_UNMASK_TARGET_WGS, read once per process, also override).
  *   attn_qt     1: split-key attention kernel (one query tile per
  *               workgroup, bf16); 2 or 4: LDS-ring kernel with that many
  *               query tiles of one KV head per workgroup; 8: 8-wave LDS ring
  *               with one query tile per wave (8 per workgroup), key-chunk
  *               partials merged by a second kernel in the same call.
- *   attn_wgs    workgroups the attention key split aims for (>= 0).
- *   unmask_wgs  workgroups the unmask vocab split aims for (>= 0).
- * Process-wide; the workspace sizes reported afterwards follow the new
- * plan, so query them again before the next call.  Not safe against
- * concurrent launches from other threads.  FDLLM_ERR_INVALID_ARG for an
- * attn_qt outside {0, 1, 2, 4, 8} or a negative target. */
+ *   attn_wgs    workgroups the attention key split aims for (0..65536).
+ *   unmask_wgs  workgroups the unmask vocab split aims for (0..65536).
+ * Per host thread: they apply to the calls and workspace queries made on
+ * the calling thread only.  The workspace sizes reported afterwards follow
+ * the new plan: query them again and re-zero a workspace sized under the
+ * old setting before reusing it (calls check the size they need).
+ * FDLLM_ERR_INVALID_ARG for an attn_qt outside {0, 1, 2, 4, 8} or a target
+ * outside [0, 65536]. */
 fdllm_status fdllm_set_tuning(int32_t attn_qt, int32_t attn_wgs, int32_t unmask_wgs);
 
 /* Planner override of the fused vocabulary projection: vocabulary tiles of
  * 32 rows per wave (1 or 2; 0 = automatic, which the environment variable
  * FDLLM_LMHEAD_VT also overrides).  Calls with more than 64 rows (batch x
- * block size) always use 1.  Process-wide; query fdllm_lmhead_unmask_workspace again
- * afterwards.  FDLLM_ERR_INVALID_ARG outside {0, 1, 2}. */
+ * block size) always use 1.  Per host thread, like fdllm_set_tuning; query
+ * fdllm_lmhead_unmask_workspace again afterwards.  FDLLM_ERR_INVALID_ARG
+ * outside {0, 1, 2}. */
 fdllm_status fdllm_set_lmhead_tuning(int32_t vt);
 
 const char* fdllm_status_string(int32_t status);

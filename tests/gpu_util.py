@@ -60,8 +60,9 @@ def nq_of(shape, mode, i):
 # attention
 # ---------------------------------------------------------------------------
 
-def run_attn(inp, ragged: bool = False, reps: int = 1):
-    """Run fdllm_block_attn on AttnInputs; returns (out float64 [b][cap][Hq][d], raw list)."""
+def run_attn(inp, ragged: bool = False, reps: int = 1, ws=None):
+    """Run fdllm_block_attn on AttnInputs; returns (out float64 [b][cap][Hq][d], raw list,
+    workspace).  `ws` reuses a caller's workspace instead of a fresh zeroed one."""
     s, mode = inp.shape, inp.mode
     keep = []
     seq = seq_for(s, ragged, keep)
@@ -71,7 +72,8 @@ def run_attn(inp, ragged: bool = False, reps: int = 1):
     kc = to_dev(inp.k_cache, s.dtype) if inp.k_cache is not None else None
     vc = to_dev(inp.v_cache, s.dtype) if inp.v_cache is not None else None
     ad = fd.attn_desc(s.n_q_heads, s.n_kv_heads, s.head_dim, fd.BF16 if s.dtype == "bf16" else fd.F32)
-    ws = fd.new_workspace(fd.block_attn_workspace(seq, ad, mode, q.shape[1]))
+    if ws is None:
+        ws = fd.new_workspace(fd.block_attn_workspace(seq, ad, mode, q.shape[1]))
     outs = []
     for _ in range(reps):
         out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)

@@ -72,7 +72,7 @@ BF = F.attn_desc(32, 32, 128, F.BF16)
     ("block_idx", _seq(block_idx=8), BF, {}, 1, "block_idx"),
     ("L>Lcap", _seq(max_seq_len=700), BF, {}, 1, "max_seq_len"),
     ("gqa", _seq(), F.attn_desc(28, 5, 128, F.BF16), {}, 1, "n_kv_heads"),
-    ("bf16 d64", _seq(), F.attn_desc(32, 32, 64, F.BF16), {}, 2, "head_dim"),
+    ("bf16 d96", _seq(), F.attn_desc(32, 32, 96, F.BF16), {}, 2, "head_dim"),
     ("f32 d96", _seq(), F.attn_desc(32, 32, 96, F.F32), {}, 2, "head_dim"),
     ("dtype", _seq(), F.attn_desc(32, 32, 128, 7), {}, 1, "dtype"),
     ("mode", _seq(), BF, {"mode": 3}, 1, "mode"),
@@ -98,6 +98,80 @@ def test_attn_workspace_query():
     assert F.block_attn_workspace(_seq(batch=0), BF, "dual", 32) == 0
     # f32 path never needs one
     assert F.block_attn_workspace(_seq(), F.attn_desc(32, 32, 128, F.F32), "dual", 32) == 0
+
+
+@pytest.mark.parametrize("mode", ["dual", "prefix", "none"])
+@pytest.mark.parametrize("shape", [
+    # (batch, Hq, Hkv, P, G, B): LLaDA-8B b1, Dream-7B b8, a small GQA case, LLaDA-8B b32 with small blocks
+    (1, 32, 32, 512, 256, 32), (8, 28, 4, 1024, 1024, 32), (2, 8, 2, 40, 96, 16), (32, 32, 32, 2048, 512, 4)])
+def test_attn_workspace_independent_of_block_index(mode, shape):
+    # One workspace, zeroed once, must serve a whole decode loop: its size
+    # (and the counter region at its start) may not depend on the block
+    # index, whose query-row count changes from block to block in prefix
+    # mode, nor on a fresh-row capacity larger than needed.
+    b, hq, hkv, P, G, B = shape
+    ad = F.attn_desc(hq, hkv, 128, F.BF16)
+    sizes = set()
+    for k in range(G // B):
+        rows = {"dual": B, "prefix": G - k * B, "none": P + G}[mode]
+        for extra in (0, 7):
+            sizes.add(F.block_attn_workspace(_seq(batch=b, max_seq_len=P + G, gen_len=G, block_size=B,
+                                                  prompt_len=P, block_idx=k), ad, mode, rows + extra))
+    assert len(sizes) == 1, sizes
+    assert sizes.pop() % 256 == 0
+
+
+def test_prefix_workspace_covers_every_block_with_counters():
+    # LLaDA-8B b1 in prefix mode splits the keys at every block index, so
+    # the workspace holds the counter region plus partials
+    ad = F.attn_desc(32, 32, 128, F.BF16)
+    n = F.block_attn_workspace(_seq(), ad, "prefix", 256)
+    counters = 1 * 32 * (256 // 32) * 4
+    assert n > counters
+
+
+def test_tuning_is_per_thread():
+    import threading
+    ad = F.attn_desc(28, 4, 128, F.BF16)
+    seq = _seq(batch=8, max_seq_len=2048, gen_len=1024, prompt_len=1024)
+    base = F.block_attn_workspace(seq, ad, "dual", 32)
+    base_u = F.unmask_workspace(_seq(batch=8), 126464, F.BF16)
+    seen = {}
+
+    def other():
+        F.set_tuning(attn_qt=2, attn_wgs=4096, unmask_wgs=4096)
+        seen["attn"] = F.block_attn_workspace(seq, ad, "dual", 32)
+        seen["unmask"] = F.unmask_workspace(_seq(batch=8), 126464, F.BF16)
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    # the other thread's plan changed, this thread's did not
+    assert seen["attn"] != base and seen["unmask"] != base_u
+    assert F.block_attn_workspace(seq, ad, "dual", 32) == base
+    assert F.unmask_workspace(_seq(batch=8), 126464, F.BF16) == base_u
+
+
+def test_set_tuning_rejects_out_of_range():
+    L = fd.lib()
+    assert L.fdllm_set_tuning(3, 0, 0) == 1
+    assert L.fdllm_set_tuning(0, -1, 0) == 1
+    assert L.fdllm_set_tuning(0, 65537, 0) == 1
+    assert L.fdllm_set_tuning(0, 0, 1 << 20) == 1
+    assert L.fdllm_set_tuning(0, 0, 0) == 0
+
+
+def test_bf16_head_dim_64_is_supported():
+    # the vector-ALU kernel serves bf16 at d = 64 (no workspace)
+    ad = F.attn_desc(8, 2, 64, F.BF16)
+    L = fd.lib()
+    seq = _seq()
+    st = L.fdllm_block_attn_workspace(ctypes.byref(seq), ctypes.byref(ad), 2, 32)
+    assert st == 0 and L.fdllm_last_error().decode() == ""
+    # validation passes up to the workspace check (none needed): reject only
+    # through a later argument, here a misaligned pointer
+    st, err = _attn_call(seq, ad, q=P1 + 2)
+    assert st == 1 and "aligned" in err
 
 
 def _unmask_call(seq, vocab=126464, dt=F.BF16, logits=P1, ss=None, rs=None, tau=0.9, flags=0, ws=P7,
@@ -175,9 +249,12 @@ def test_set_tuning_rejects_and_replans():
     finally:
         fd.set_tuning()
     assert one == 0 and many > 0  # one key chunk needs no partials
-    # 8 key chunks of partials for 8 x 28 heads x 32 rows: O in fp16 (256 bytes
-    # per row), then m, l and the row scale in fp32
-    assert one8 == 0 and auto8 == 8 * 28 * 8 * (32 * 128 * 2 + 3 * 32 * 4)
+    # the counter region (one 4-byte counter per sequence, head and query
+    # tile, rounded up to 256 bytes), then 8 key chunks of partials for 8 x
+    # 28 heads x 32 rows: O in fp16 (256 bytes per row), then m, l and the
+    # row scale in fp32
+    counters = (8 * 28 * 1 * 4 + 255) // 256 * 256
+    assert one8 == 0 and auto8 == counters + 8 * 28 * 8 * (32 * 128 * 2 + 3 * 32 * 4)
 
 
 def _lm_call(seq, vocab=126464, hidden=4096, x=P1, ss=None, rs=None, wp=P2, tau=0.9, k=None, flags=0, ws=P7,
