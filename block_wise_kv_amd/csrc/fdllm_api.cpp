@@ -349,6 +349,7 @@ size_t fdllm_block_attn_workspace(const fdllm_seq_desc* seq, const fdllm_attn_de
                                   int32_t fresh_rows) {
   AttnSetup su;
   if (setup_attn(seq, attn, mode, fresh_rows, su)) return 0;
+  ok();
   return su.ws_geometry;
 }
 
@@ -404,6 +405,7 @@ fdllm_status fdllm_block_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
 size_t fdllm_unmask_workspace(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype) {
   UnmaskSetup su;
   if (setup_unmask(seq, vocab, logits_dtype, su)) return 0;
+  ok();
   return su.ws;
 }
 
@@ -487,6 +489,7 @@ fdllm_status fdllm_unmask_topk(const fdllm_seq_desc* seq, int32_t vocab, int32_t
 
 size_t fdllm_lmhead_packed_bytes(int32_t vocab, int32_t hidden) {
   if (check_lmhead_dims(vocab, hidden)) return 0;
+  ok();
   return lmhead_packed_bytes(vocab, hidden);
 }
 
@@ -509,6 +512,7 @@ fdllm_status fdllm_lmhead_pack(int32_t vocab, int32_t hidden, const void* w, voi
 size_t fdllm_lmhead_unmask_workspace(const fdllm_seq_desc* seq, int32_t vocab, int32_t hidden) {
   LmheadSetup su;
   if (setup_lmhead(seq, vocab, hidden, su)) return 0;
+  ok();
   return su.ws;
 }
 
