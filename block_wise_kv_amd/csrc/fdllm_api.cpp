@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <string>
 
 #include "fdllm.h"
@@ -411,6 +412,64 @@ size_t fdllm_unmask_workspace(const fdllm_seq_desc* seq, int32_t vocab, int32_t 
 
 }  // extern "C"
 
+// ---- scratch of the allocation-free threshold unmask
+// (fdllm_unmask_threshold_static).  One array per device, held until the
+// process ends: the arrival counters first, at offsets that do not depend
+// on the batch (the finished-sequence counter at 0, the per-sequence
+// arrival counters at 256, the per-sequence done flags at 32 KB: counters
+// that must read zero never overlap a word another call left non-zero),
+// then the vocabulary-chunk partials.  The kernels reset every counter they
+// use, so after one clear per device the array stays ready for the next
+// call.  Calls that overlap on one device share it and race.
+namespace {
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+constexpr size_t kStaticCounterBytes = (size_t)64 << 10;
+constexpr int kStaticMaxBatch = 4096;
+constexpr size_t kStaticSeqCntOffset = 256;
+constexpr size_t kStaticDoneFlagOffset = (size_t)32 << 10;
+static_assert(kStaticSeqCntOffset + 4 * (size_t)kStaticMaxBatch <= kStaticDoneFlagOffset, "counter layout");
+static_assert(kStaticDoneFlagOffset + 8 * (size_t)kStaticMaxBatch <= kStaticCounterBytes, "counter layout");
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch` on each device (null: not set up)
+
+// Bind the unmask arguments to this device's copy of `scratch`.  The first
+// call on a device looks up the array's device address (the host-side name
+// is only a stand-in) and clears its counter region with a fill kernel on
+// `stream`, ordered before this call's kernel.
+fdllm_status bind_static_scratch(UnmaskArgs& a, void* stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FDLLM_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  void* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(FDLLM_ERR_LAUNCH, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      e = launch_fill_zero(p, kStaticCounterBytes, (hipStream_t)stream);
+      if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "scratch clear failed: %s", hipGetErrorString(e));
+      g_scratch_ptr[dev] = p;
+    }
+    base = g_scratch_ptr[dev];
+  }
+  char* w = (char*)base;
+  a.glob = (uint64_t*)w;
+  a.seq_cnt = (uint32_t*)(w + kStaticSeqCntOffset);
+  a.done_flag = (int32_t*)(w + kStaticDoneFlagOffset);
+  a.part = (UnmaskPartial*)(w + kStaticCounterBytes);
+  return FDLLM_OK;
+}
+}  // namespace
+
 namespace {
 // The threshold rule (topk == 0) and the fixed-step rule (topk > 0) share
 // the vocabulary pass and differ only in the selection of the finalisation.
@@ -418,7 +477,7 @@ fdllm_status run_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits
                         int64_t seq_stride, int64_t row_stride, float threshold, int32_t topk, uint32_t flags,
                         int32_t* tokens, uint8_t* mask, int32_t* n_decoded, int32_t* decoded_pos, double* conf,
                         int32_t* done_seqs, int32_t* n_done, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, bool use_static = false) {
   UnmaskSetup su;
   fdllm_status st = setup_unmask(seq, vocab, logits_dtype, su);
   if (st) return st;
@@ -431,10 +490,21 @@ fdllm_status run_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits
   if (seq->batch > 1 && seq_stride < (int64_t)(seq->block_size - 1) * row_stride + vocab)
     return fail(FDLLM_ERR_INVALID_ARG, "seq_stride %lld overlaps the rows of the previous sequence",
                 (long long)seq_stride);
-  if (!workspace || workspace_bytes < su.ws)
-    return fail(FDLLM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", su.ws,
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned16(workspace)) return fail(FDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (use_static) {
+    const size_t part = (size_t)seq->batch * seq->block_size * su.nchunk * sizeof(UnmaskPartial);
+    if (seq->batch > kStaticMaxBatch)
+      return fail(FDLLM_ERR_UNSUPPORTED, "batch %d exceeds the static scratch's limit of %d sequences", seq->batch,
+                  kStaticMaxBatch);
+    if (part > kStaticScratchBytes - kStaticCounterBytes)
+      return fail(FDLLM_ERR_UNSUPPORTED,
+                  "batch x block_size x vocab chunks needs %zu bytes of partials; the static scratch holds %zu",
+                  part, kStaticScratchBytes - kStaticCounterBytes);
+  } else {
+    if (!workspace || workspace_bytes < su.ws)
+      return fail(FDLLM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", su.ws,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(FDLLM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
   st = debug_validate(su.sa, su.max_P, nullptr, nullptr, stream);
   if (st) return st;
   const size_t es = logits_dtype == FDLLM_BF16 ? 2 : 4;
@@ -458,7 +528,12 @@ fdllm_status run_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits
   a.n_done = n_done;
   a.nchunk = su.nchunk;
   a.chunk = su.chunk;
-  unmask_bind_workspace(a, workspace);
+  if (use_static) {
+    st = bind_static_scratch(a, stream);
+    if (st) return st;
+  } else {
+    unmask_bind_workspace(a, workspace);
+  }
   hipError_t e = launch_unmask(a, logits_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "unmask launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -475,6 +550,16 @@ fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, in
   if (isnan(threshold)) return fail(FDLLM_ERR_INVALID_ARG, "threshold is NaN");
   return run_unmask(seq, vocab, logits_dtype, logits, seq_stride, row_stride, threshold, 0, flags, tokens, mask,
                     n_decoded, decoded_pos, conf, done_seqs, n_done, workspace, workspace_bytes, stream);
+}
+
+fdllm_status fdllm_unmask_threshold_static(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype,
+                                           const void* logits, int64_t seq_stride, int64_t row_stride,
+                                           float threshold, uint32_t flags, int32_t* tokens, uint8_t* mask,
+                                           int32_t* n_decoded, int32_t* decoded_pos, double* conf,
+                                           int32_t* done_seqs, int32_t* n_done, void* stream) {
+  if (isnan(threshold)) return fail(FDLLM_ERR_INVALID_ARG, "threshold is NaN");
+  return run_unmask(seq, vocab, logits_dtype, logits, seq_stride, row_stride, threshold, 0, flags, tokens, mask,
+                    n_decoded, decoded_pos, conf, done_seqs, n_done, nullptr, 0, stream, true);
 }
 
 fdllm_status fdllm_unmask_topk(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype, const void* logits,

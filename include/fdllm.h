@@ -183,6 +183,27 @@ fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, in
                                     int32_t* done_seqs, int32_t* n_done,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* fdllm_unmask_threshold without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, rule, outputs and
+ * kernels as fdllm_unmask_threshold minus workspace / workspace_bytes: the
+ * arrival counters and vocabulary-chunk partials live in a static scratch
+ * array of the library (8 MiB per device, held until the process ends; the
+ * first call on a device finds its address and clears its counters with a
+ * fill kernel on `stream`).  Limits: batch <= 4096 and batch x block_size x
+ * vocabulary chunks x 16 bytes <= 8 MiB - 64 KiB (a call beyond them returns
+ * FDLLM_ERR_UNSUPPORTED and launches nothing).  Every call on a device
+ * shares that device's scratch: calls that overlap in time on one device
+ * (different streams without ordering, or several host threads) race and
+ * must not be issued; the first call on a device must be ordered before
+ * calls on other streams.  Allocates nothing, synchronises nothing. */
+fdllm_status fdllm_unmask_threshold_static(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype,
+                                           const void* logits, int64_t seq_stride, int64_t row_stride,
+                                           float threshold, uint32_t flags,
+                                           int32_t* tokens, uint8_t* mask, int32_t* n_decoded,
+                                           int32_t* decoded_pos, double* conf,
+                                           int32_t* done_seqs, int32_t* n_done, void* stream);
+
 /* One step of fixed-step decoding ([README] "Usage": a fixed number of
  * sampling steps, so a fixed number of tokens per step -- the decoding the
  * evaluation table's "LLaDA" and "+cache" columns use).  Same vocabulary

@@ -161,6 +161,24 @@ def test_set_tuning_rejects_out_of_range():
     assert L.fdllm_set_tuning(0, 0, 0) == 0
 
 
+def test_static_unmask_rejects_beyond_its_scratch():
+    # validated on the host before the scratch is touched: nothing launches
+    L = fd.lib()
+    seq = _seq(batch=4097)
+    st = L.fdllm_unmask_threshold_static(ctypes.byref(seq), 126464, F.BF16, P1, 32 * 126464, 126464, 0.9, 0,
+                                         P2, P3, P4, None, None, None, None, None)
+    assert st == 2 and "static scratch" in L.fdllm_last_error().decode()
+    # 1024 sequences x 1024 block rows x one vocabulary chunk x 16 bytes of
+    # partials = 16 MiB, beyond the 8 MiB scratch
+    seq = _seq(batch=1024, block_size=1024, gen_len=1024, max_seq_len=2048)
+    st = L.fdllm_unmask_threshold_static(ctypes.byref(seq), 126464, F.BF16, P1, 1024 * 126464, 126464, 0.9, 0,
+                                         P2, P3, P4, None, None, None, None, None)
+    assert st == 2 and "partials" in L.fdllm_last_error().decode()
+    st = L.fdllm_unmask_threshold_static(ctypes.byref(_seq()), 126464, F.BF16, P1, 32 * 126464, 126464,
+                                         float("nan"), 0, P2, P3, P4, None, None, None, None, None)
+    assert st == 1
+
+
 def test_bf16_head_dim_64_is_supported():
     # the vector-ALU kernel serves bf16 at d = 64 (no workspace)
     ad = F.attn_desc(8, 2, 64, F.BF16)
