@@ -1016,12 +1016,13 @@ __global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_r
 // later), so no workgroup has to read a whole group's partials.
 constexpr int kGqaWaves = 8;
 constexpr int kGqaThreads = 64 * kGqaWaves;
+constexpr int kNumCUs = 256;  // MI355X compute units: one persistent 8-wave workgroup each
 template <int NR>
 __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   constexpr int QPW = kGqaWaves;                    // query tiles per workgroup
   constexpr int SET = 2 * kTileBytes;               // ring set: one tile of K then V
   constexpr int DPR = 2;                            // 1 KB loads per wave per round
-  static_assert(NR == 4, "four ring sets: the pipeline reads two per round; the epilogue needs 64 KB");
+  static_assert(NR == 4 || NR == 6 || NR == 8, "an even number of ring sets, at least four (the epilogue needs 64 KB)");
   // One array per ring set: the compiler then tells the sets apart, so its
   // LDS reads of one set are not held behind the LDS-DMA loads still in
   // flight into another, and it schedules them like any LDS load.
@@ -1029,12 +1030,20 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring1[SET];
   __shared__ __attribute__((aligned(16))) uint8_t ring2[SET];
   __shared__ __attribute__((aligned(16))) uint8_t ring3[SET];
+  __shared__ __attribute__((aligned(16))) uint8_t ring4[NR > 4 ? SET : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ring5[NR > 4 ? SET : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ring6[NR > 6 ? SET : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ring7[NR > 6 ? SET : 16];
   auto set_ptr = [&](auto jc) __attribute__((always_inline)) -> uint8_t* {
     constexpr int J = decltype(jc)::value % NR;
     if constexpr (J == 0) return ring0;
     if constexpr (J == 1) return ring1;
     if constexpr (J == 2) return ring2;
-    return ring3;
+    if constexpr (J == 3) return ring3;
+    if constexpr (J == 4) return ring4;
+    if constexpr (J == 5) return ring5;
+    if constexpr (J == 6) return ring6;
+    return ring7;
   };
 
   const int bid = blockIdx.x;
@@ -1125,8 +1134,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
     } else {
       const int j = min(t0 + row_a, g.ke - 1);
       __builtin_amdgcn_global_load_lds((const char*)kv_row(a, knp, kcp, g, j, kD) + 16 * chunk_a, dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const char*)kv_row(a, vnp, vcp, g, j, kD) + 16 * chunk_a, dst + kTileBytes, 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds((const char*)kv_row(a, vnp, vcp, g, j, kD) + 16 * chunk_a, dst + kTileBytes, 16, 0, 0);
     }
   };
 
@@ -1246,6 +1254,8 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   issue(2, std::integral_constant<int, 2>{});
   if constexpr (NR > 4) issue(3, std::integral_constant<int, 3>{});
   if constexpr (NR > 5) issue(4, std::integral_constant<int, 4>{});
+  if constexpr (NR > 6) issue(5, std::integral_constant<int, 5>{});
+  if constexpr (NR > 7) issue(6, std::integral_constant<int, 6>{});
   wait_vm<(NR - 2) * DPR, true>();
   ring_barrier();
   if (live) stage_s(ring0, Sb[0]);
@@ -1256,6 +1266,8 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
     step(q + 3, std::integral_constant<int, 3>{});
     if constexpr (NR > 4) step(q + 4, std::integral_constant<int, 4>{});
     if constexpr (NR > 5) step(q + 5, std::integral_constant<int, 5>{});
+    if constexpr (NR > 6) step(q + 6, std::integral_constant<int, 6>{});
+    if constexpr (NR > 7) step(q + 7, std::integral_constant<int, 7>{});
   }
   wait_vm<0, true>();
   ring_barrier();
@@ -1350,6 +1362,619 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(AttnArgs a) {
     case 6: merge_partials16_n<6, 1>(r, cq, j, c, orow, c0); break;
     case 7: merge_partials16_n<7, 1>(r, cq, j, c, orow, c0); break;
     default: merge_partials16_n<8, 1>(r, cq, j, c, orow, c0); break;
+  }
+}
+
+// ------------------------------------------------------------------ bf16 MFMA, 8-wave ring over a stream of tiles
+// The 8-wave ring for DualCache GQA batches (one query tile per head), with
+// the key tiles of the whole batch dealt evenly over a persistent grid.  The
+// tiles of sequence i's KV head hk form segment (i, hk), n_i = ceil(L_i / 32)
+// tiles long; the segments laid end to end (sequence-major, KV head within
+// a sequence) are cut into gridDim.x equal ranges, one per workgroup.  A
+// ragged batch (prompts of 256 to 4096 tokens) then costs every workgroup
+// the same number of tiles instead of the longest sequence's.  A workgroup
+// walks the segments its range touches: a segment wholly inside the range
+// is written to the output directly; a segment cut by range edges is
+// computed in parts, whose (O, m, l) partials (the fp16 format of the
+// split-key kernel, written through to the device coherence point) go to
+// two slots per workgroup in the workspace, and the part that arrives last
+// merges them in a fixed order.  Every workgroup derives the partition from
+// the prompt lengths itself, so the call stays one launch with no host pass.
+// Tiles of sequence i's segment in the tile stream: ceil(L_i / 32) rounded
+// up to a multiple of 4, so that segments and ranges start on 4-tile
+// boundaries (the padding tiles hold no keys: their loads re-read the
+// segment's last row and their compute is skipped).
+constexpr int kStreamQuad = 4;
+__device__ __forceinline__ int seq_tiles_sq(const SeqArgs& sq, int i) {
+  const int n = (seq_prompt(sq, i) + sq.G + kKT - 1) / kKT;
+  return (n + kStreamQuad - 1) / kStreamQuad * kStreamQuad;
+}
+__device__ __forceinline__ int seq_tiles(const AttnArgs& a, int i) {
+  const int n = (seq_prompt(a.sq, i) + a.sq.G + kKT - 1) / kKT;
+  return (n + kStreamQuad - 1) / kStreamQuad * kStreamQuad;
+}
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+// A value the caller knows to be the same in every lane, moved to scalar
+// registers (so that what is computed from it stays scalar: branches,
+// per-sequence lookups as scalar loads).
+__device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long uniform_ll(long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(unsigned long long)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+// The ranges are cut in whole quads of 4 tiles: with TQ = T / 4 quads,
+// range u is quads [u TQ / G, (u + 1) TQ / G).  stream_lo is a range's
+// first tile; stream_owner the range holding tile x.
+__device__ __forceinline__ long long stream_lo(int u, long long T, int G) {
+  return (long long)u * (T / kStreamQuad) / G * kStreamQuad;
+}
+__device__ __forceinline__ int stream_owner(long long x, long long T, int G) {
+  const long long xq = x / kStreamQuad, TQ = T / kStreamQuad;
+  return (int)((xq * G + G - 1) / TQ);
+}
+
+// A workgroup's place in its tile range: the segment (sequence i, KV head
+// hk), the tile t within it, this workgroup's part of the segment [tb, te),
+// the global tile index x, and the segment's geometry.  Wave-uniform.
+struct StreamCursor {
+  int i, hk, t, tb, te, n;
+  long long x;
+  int L, a0, a1, ke;
+  const char *kc, *vc, *kf, *vf;  // row 0 of the segment's cached and fresh K / V
+};
+
+template <int NR>
+__global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArgs a) {
+  constexpr int SET = 2 * kTileBytes;
+  constexpr int DPR = 2;   // ring loads per wave per tile
+  constexpr int QLD = 8;   // Q-prefetch loads per wave (32 rows x 256 bytes)
+  static_assert(NR == 4, "four ring sets");
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[SET];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[SET];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[SET];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[SET];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kGqaWaves * kQT * 256];  // each wave's next Q tile
+  __shared__ __attribute__((aligned(16))) uint8_t q_sink[kGqaWaves * 1024];      // never read (see prefetch_none)
+  auto set_ptr = [&](auto jc) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int J = decltype(jc)::value % NR;
+    if constexpr (J == 0) return ring0;
+    if constexpr (J == 1) return ring1;
+    if constexpr (J == 2) return ring2;
+    return ring3;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lq = lane & 31, hh = lane >> 5;
+  // XCD-aware: blockIdx.x is dealt round-robin over the 8 XCDs; give each
+  // XCD a contiguous run of ranges
+  const int w = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  // the arguments the loop reads, as plain scalars (reads through the
+  // argument block inside the loop would each wait for every load in flight)
+  const int32_t* plens = a.sq.plens;
+  const int32_t* bidxp = a.sq.bidx;
+  const int b = a.sq.b, Pu = a.sq.P, Ku = a.sq.k, Gl = a.sq.G, Bl = a.sq.B, Lcap = a.sq.Lcap;
+  const int Hkv = a.Hkv, Hq = a.Hq, gg = a.g, fresh_rows = a.fresh_rows, mode = a.mode;
+  const float c = a.scale_log2;
+  const uint16_t* qp = (const uint16_t*)a.q;
+  uint16_t* outp = (uint16_t*)a.out;
+  uint8_t* partp = (uint8_t*)a.part;
+  // per-sequence lookups, uniform (the sequence index is)
+  // (scalar loads through the constant address space: they wait on the
+  // scalar counter only, not on the ring's loads in flight)
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+  auto prompt_of = [&](int i) __attribute__((always_inline)) -> int {
+    return plens ? ((ConstI32)plens)[uniform_i(i)] : Pu;
+  };
+  auto block_of = [&](int i) __attribute__((always_inline)) -> int {
+    return bidxp ? ((ConstI32)bidxp)[uniform_i(i)] : Ku;
+  };
+  auto tiles_of_len = [](int L) -> int { return (L + kKT * kStreamQuad - 1) / (kKT * kStreamQuad) * kStreamQuad; };
+
+  // ---- the partition (every wave computes it; the results are uniform).
+  // With fewer quads than workgroups only the first TQ take part, so every
+  // range holds at least one quad and consecutive owners are consecutive
+  // workgroups (attn_stream_merge_kernel's part count relies on it).
+  long long total = 0;
+  for (int i0 = 0; i0 < b; i0 += 64) {
+    const int n = i0 + lane < b ? tiles_of_len((plens ? plens[i0 + lane] : Pu) + Gl) : 0;
+    total += __shfl(wave_scan_incl(n), 63, 64);
+  }
+  const long long T = uniform_ll(total * a.Hkv);
+  const long long TQ = T / kStreamQuad;
+  const int Gn = (int)((long long)gridDim.x < TQ ? (long long)gridDim.x : TQ);
+  if (w >= Gn) return;
+  const long long lo = stream_lo(w, T, Gn), hi = stream_lo(w + 1, T, Gn);
+  int i_lo = 0;
+  long long base = 0;  // global index of sequence i_lo's first tile
+  for (int i0 = 0; i0 < b; i0 += 64) {
+    const bool in = i0 + lane < b;
+    const int n = in ? tiles_of_len((plens ? plens[i0 + lane] : Pu) + Gl) : 0;
+    const int incl = wave_scan_incl(n);
+    const uint64_t m = __ballot(in && base + (long long)Hkv * incl > lo);
+    if (m) {
+      const int f = __ffsll((unsigned long long)m) - 1;
+      i_lo = i0 + f;
+      base += (long long)Hkv * __shfl(incl - n, f, 64);
+      break;
+    }
+    base += (long long)Hkv * __shfl(incl, 63, 64);
+  }
+
+  // segment geometry of a cursor that has just entered segment (i, hk) at tile t
+  auto enter = [&](StreamCursor& cu) __attribute__((always_inline)) {
+    const int P = prompt_of(cu.i);
+    cu.L = P + Gl;
+    fresh_range(mode, P, Gl, Bl, block_of(cu.i), cu.a0, cu.a1);
+    cu.n = tiles_of_len(cu.L);
+    cu.tb = cu.t;
+    cu.te = (int)min((long long)cu.n, (long long)cu.t + (hi - cu.x));
+    cu.ke = max(min(cu.L, cu.te * kKT), cu.tb * kKT + 1);  // at least one key row to clamp to
+    const size_t cb = ((size_t)cu.i * Hkv + cu.hk) * Lcap * 256;
+    const size_t fb = ((size_t)cu.i * fresh_rows * Hkv + cu.hk) * 256;
+    cu.kc = (const char*)a.kc + cb;
+    cu.vc = (const char*)a.vc + cb;
+    cu.kf = (const char*)a.kn + fb;
+    cu.vf = (const char*)a.vn + fb;
+  };
+  // one tile on: past the part's end the cursor enters the next segment
+  // (while the range lasts; past it, it stays on its last tile)
+  auto advance = [&](StreamCursor& cu) __attribute__((always_inline)) {
+    if (cu.x + 1 >= hi) {
+      cu.x = hi;
+      return;
+    }
+    ++cu.x;
+    if (++cu.t == cu.te) {
+      cu.t = 0;
+      if (++cu.hk == Hkv) {
+        cu.hk = 0;
+        ++cu.i;
+      }
+      enter(cu);
+    }
+  };
+  i_lo = uniform_i(i_lo);
+  base = uniform_ll(base);
+  StreamCursor ic;  // issue cursor, three tiles ahead of the compute cursor
+  {
+    const int n0 = tiles_of_len(prompt_of(i_lo) + Gl);
+    ic.i = i_lo;
+    ic.hk = (int)((lo - base) / n0);
+    ic.t = (int)((lo - base) % n0);
+    ic.x = lo;
+    enter(ic);
+  }
+  StreamCursor cc = ic;  // compute cursor
+
+  // K/V tile at the issue cursor into ring set J: wave w moves rows 4 w +
+  // [0, 4) of K and of V (one 1 KB LDS-DMA load each); this lane moves the
+  // 16-byte chunk that belongs at its LDS position under the ring swizzle.
+  // Rows past the part (and every tile once the cursor is past the range)
+  // re-read the part's last row, so every step issues the same loads.
+  const int row_a = 4 * wid + (lane >> 4);
+  const int chunk_a = (lane & 15) ^ ring_swizzle(row_a);
+  const size_t fstride = (size_t)Hkv * 256;
+  const uint32_t off_c = (uint32_t)(row_a * 256 + 16 * chunk_a);
+  const uint32_t off_f = (uint32_t)(row_a * Hkv * 256 + 16 * chunk_a);
+  auto issue = [&](auto jc) __attribute__((always_inline)) {
+    uint8_t* dst = set_ptr(jc) + wid * 1024;
+    // (hidden from alias analysis: the compiler otherwise takes the reads of
+    // the other ring sets in this step as depending on these loads and waits
+    // for all of them; the explicit waits above order every hand-off)
+    asm volatile("" : "+s"(dst));
+    const int t0 = (ic.x < hi ? ic.t : ic.te - 1) * kKT;
+    const bool whole = t0 + kKT <= ic.ke;
+    const bool in_cache = whole && (t0 + kKT <= ic.a0 || t0 >= ic.a1);
+    const bool in_fresh = whole && t0 >= ic.a0 && t0 + kKT <= ic.a1;
+    if (in_cache || in_fresh) {
+      const char* kt = in_cache ? ic.kc + (size_t)t0 * 256 + off_c : ic.kf + (size_t)(t0 - ic.a0) * fstride + off_f;
+      const char* vt = in_cache ? ic.vc + (size_t)t0 * 256 + off_c : ic.vf + (size_t)(t0 - ic.a0) * fstride + off_f;
+      __builtin_amdgcn_global_load_lds(kt, dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vt, dst + kTileBytes, 16, 0, 0);
+    } else {
+      const int j = min(t0 + row_a, ic.ke - 1);
+      const bool fr = (unsigned)(j - ic.a0) < (unsigned)(ic.a1 - ic.a0);
+      const char* kt = fr ? ic.kf + (size_t)(j - ic.a0) * fstride : ic.kc + (size_t)j * 256;
+      const char* vt = fr ? ic.vf + (size_t)(j - ic.a0) * fstride : ic.vc + (size_t)j * 256;
+      __builtin_amdgcn_global_load_lds(kt + 16 * chunk_a, dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vt + 16 * chunk_a, dst + kTileBytes, 16, 0, 0);
+    }
+  };
+  // This wave's Q tile of the segment after the compute cursor's current one
+  // (query head hk * g + wid of that segment) into its 8 KB of q_lds: row r
+  // of the tile, 16-byte chunk k at chunk k ^ (r & 15) (conflict-free reads
+  // below); rows past the block re-read its last row (zeroed on reading).
+  // QLD loads per wave, whatever the wave or segment.
+  auto prefetch_q = [&](int i, int hk) __attribute__((always_inline)) {
+    const int P = prompt_of(i);
+    int a0, a1;
+    fresh_range(mode, P, Gl, Bl, block_of(i), a0, a1);
+    const int nq = a1 - a0;
+    const int h = hk * gg + min(wid, gg - 1);
+    uint8_t* dst = q_lds + wid * (kQT * 256);
+#pragma unroll
+    for (int v = 0; v < QLD; ++v) {
+      const int r = 4 * v + (lane >> 4);
+      const int k = (lane & 15) ^ (r & 15);
+      const uint16_t* src = qp + (((size_t)i * fresh_rows + max(min(r, nq - 1), 0)) * Hq + h) * kD;
+      __builtin_amdgcn_global_load_lds((const char*)src + 16 * k, dst + v * 1024, 16, 0, 0);
+    }
+  };
+  // The same number of loads with nothing to fetch: every lane copies the
+  // first 16 bytes of Q into this wave's KB of q_sink.  Every quad of steps
+  // issues QLD Q-side loads per wave, a prefetch or these, so the count of
+  // loads in flight at each wait is the same on every path.
+  auto prefetch_none = [&]() __attribute__((always_inline)) {
+    uint8_t* dst = q_sink + wid * 1024;
+#pragma unroll
+    for (int v = 0; v < QLD; ++v) __builtin_amdgcn_global_load_lds((const char*)qp, dst, 16, 0, 0);
+  };
+  // Q as the B operand of S^T = K Q^T from q_lds: lane (lq, hh) holds query
+  // row lq, columns [16 ks + 8 hh, +8) for ks = 0..7; rows past nq are zero
+  bf16x8 qop[8];
+  auto read_q = [&](int nq) __attribute__((always_inline)) {
+    const uint8_t* src = q_lds + wid * (kQT * 256) + lq * 256;
+    const bool rl = lq < nq;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 v = *(const uint4*)(src + 16 * ((2 * ks + hh) ^ (lq & 15)));
+      qop[ks] = as_bf16x8(rl ? v : make_uint4(0, 0, 0, 0));
+    }
+  };
+
+  // operand addresses within a tile (as in the LDS ring kernel)
+  uint32_t k_off[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) k_off[ks] = (uint32_t)(lq * 256 + 16 * ((2 * ks + hh) ^ ring_swizzle(lq)));
+  uint32_t vt_off[8];
+  {
+    const int G = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int hi2 = 0; hi2 < 2; ++hi2) {
+        const int r = 4 * (G >> 1) + (sl >> 2) + 8 * hi2;
+        const int col = 32 * dt + 16 * (G & 1) + 4 * (sl & 3);
+        vt_off[2 * dt + hi2] = (uint32_t)(r * 256 + 16 * ((col >> 3) ^ ring_swizzle(r)) + 8 * ((col >> 2) & 1));
+      }
+  }
+
+  const bool live = wid < gg;  // wave wid owns query head hk * g + wid
+  f32x16 O[4];
+  float m_ref, l_run;
+  auto reset = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[dt][r] = 0.f;
+    m_ref = -INFINITY;
+    l_run = 0.f;
+  };
+  reset();
+
+  auto stage_s = [&](const uint8_t* tb, f32x16& S) __attribute__((always_inline)) {
+    bf16x8 kop[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kop[ks] = as_bf16x8(*(const uint4*)(tb + k_off[ks]));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(kop[ks]));
+    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qop[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int ks = 1; ks < 8; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], S, 0, 0, 0);
+  };
+  auto stage_pv = [&](const uint8_t* tb, int t0, int ke, f32x16& S) __attribute__((always_inline)) {
+    bf16x8 vop[2][4];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        typedef __attribute__((address_space(3))) short4v* LdsS4;
+        const uint8_t* vb = tb + kTileBytes + 16 * 256 * k2;
+        const short4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS4)(vb + vt_off[2 * dt]));
+        const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS4)(vb + vt_off[2 * dt + 1]));
+        __builtin_memcpy(&vop[k2][dt], &v0, 8);
+        __builtin_memcpy((char*)&vop[k2][dt] + 8, &v1, 8);
+      }
+    if (t0 + kKT > ke) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = t0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key >= ke) S[r] = -INFINITY;
+      }
+    }
+    float mx = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+    mx = xor_combine<32>(mx, [](float x, float y) { return fmaxf(x, y); });
+    if (__ballot((mx - m_ref) * c > kRefSlack)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = exp2_fast((m_ref - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float mc = m_ref * c;
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = exp2_fast(fmaf(S[r], c, -mc));
+    l_run += pairwise_sum16(p);
+    bf16x8 pop[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      uint4 u;
+      u.x = cvt_pk_bf16(p[8 * h2 + 0], p[8 * h2 + 1]);
+      u.y = cvt_pk_bf16(p[8 * h2 + 2], p[8 * h2 + 3]);
+      u.z = cvt_pk_bf16(p[8 * h2 + 4], p[8 * h2 + 5]);
+      u.w = cvt_pk_bf16(p[8 * h2 + 6], p[8 * h2 + 7]);
+      pop[h2] = as_bf16x8(u);
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[k2][dt], pop[k2], O[dt], 0, 0, 0);
+  };
+
+  // The end of the compute cursor's part: the output rows when the part is
+  // the whole segment, else the partial (O, m, l: fp16 O with a power-of-two
+  // row scale) in slot (w, first ? 0 : 1): a workgroup's first segment holds
+  // its range start, a later cut segment its range end.  Stores straight
+  // from the accumulator layout (lane (lq, hh): row lq, head dims 32 dt +
+  // 8 q4 + 4 hh + [0, 4)).
+  auto finish = [&](bool first) __attribute__((always_inline)) {
+    if (!live) return;
+    const int h = cc.hk * gg + wid;
+    const int nq = cc.a1 - cc.a0;
+    const float l_col = xor_combine<32>(l_run, [](float x, float y) { return x + y; });
+    if (cc.tb == 0 && cc.te == cc.n) {
+      if (lq < nq) {
+        const float inv = 1.f / l_col;
+        uint16_t* orow = outp + (((size_t)cc.i * fresh_rows + lq) * Hq + h) * kD;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            uint2 u;
+            u.x = pack_bf16x2(O[dt][4 * r4 + 0] * inv, O[dt][4 * r4 + 1] * inv);
+            u.y = pack_bf16x2(O[dt][4 * r4 + 2] * inv, O[dt][4 * r4 + 3] * inv);
+            *(uint2*)(orow + 32 * dt + 8 * r4 + 4 * hh) = u;
+          }
+      }
+      return;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(O[dt][r]));
+    amax = xor_combine<32>(amax, [](float x, float y) { return fmaxf(x, y); });
+    const int e = __builtin_amdgcn_frexp_expf(amax) - 15;  // amax < 2^(e + 15)
+    uint8_t* part = partp + ((size_t)(2 * w + (first ? 0 : 1)) * kGqaWaves + wid) * kPart16Bytes;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint2 u;
+        u.x = pack_f16x2(__builtin_amdgcn_ldexpf(O[dt][4 * q4], -e), __builtin_amdgcn_ldexpf(O[dt][4 * q4 + 1], -e));
+        u.y = pack_f16x2(__builtin_amdgcn_ldexpf(O[dt][4 * q4 + 2], -e), __builtin_amdgcn_ldexpf(O[dt][4 * q4 + 3], -e));
+        *(uint2*)(part + lq * 256 + 2 * (32 * dt + 8 * q4 + 4 * hh)) = u;
+      }
+    if (hh == 0) {
+      float* hdr = (float*)(part + kQT * kD * 2);
+      hdr[lq] = m_ref;
+      hdr[kQT + lq] = l_col;
+      hdr[2 * kQT + lq] = __builtin_amdgcn_ldexpf(1.f, e);
+    }
+  };
+
+  // ---- the pipeline.  Step x (the compute cursor's tile): wait until tile
+  // x + 1 is in (later tiles may stay in flight), barrier, refill the ring
+  // set tile x - 1 used with the issue cursor's tile x + 3, start S^T of
+  // tile x + 1 when it is in the same segment, finish tile x (softmax and
+  // P V).  After each quad of steps: at the end of a segment part, write its
+  // output or partial, take the next segment's Q from q_lds and start S^T of
+  // its first tile; then QLD Q-side loads (the following segment's Q when a
+  // segment has just been entered, else prefetch_none).  Those loads are
+  // younger than tiles x + 1 and x + 2 at the first two steps of a quad (the
+  // waits there leave them in flight) and older than the tiles waited for at
+  // the last two, so a prefetch has landed one quad after it was issued, and
+  // a segment part spans at least one quad.
+  f32x16 Sb[2] = {f32x16{}, f32x16{}};
+  bool first = true;  // the compute cursor is in this workgroup's first segment
+  // the segment after the compute cursor's current one (if the range reaches it)
+  auto next_seg = [&](int& i2, int& hk2) __attribute__((always_inline)) -> bool {
+    if (cc.x + (cc.te - cc.t) >= hi) return false;
+    i2 = cc.i;
+    hk2 = cc.hk + 1;
+    if (hk2 == Hkv) {
+      hk2 = 0;
+      ++i2;
+    }
+    return true;
+  };
+  auto step = [&](auto jc) __attribute__((always_inline)) {
+    constexpr int J = decltype(jc)::value;
+    wait_vm<(NR - 3) * DPR + (J < 2 ? QLD : 0), true>();
+    ring_barrier();
+    issue(std::integral_constant<int, (J + NR - 1) % NR>{});
+    advance(ic);
+    if (cc.x >= hi) return;  // past the range: the loads above keep the counts exact
+    // segment parts are whole quads: tile x + 1 leaves the part only after
+    // the quad's last step, which boundary() handles
+    const bool more = J < NR - 1 || cc.t + 1 < cc.te;
+    const bool keys = cc.t * kKT < cc.L;  // a padding tile holds none
+    if (live && more && (cc.t + 1) * kKT < cc.L)
+      stage_s(set_ptr(std::integral_constant<int, (J + 1) % NR>{}), Sb[(J + 1) & 1]);
+    if (live && keys) stage_pv(set_ptr(jc), cc.t * kKT, cc.ke, Sb[J & 1]);
+    if (more) advance(cc);
+  };
+  auto boundary = [&]() __attribute__((always_inline)) {
+    bool entered = false;
+    if (cc.x < hi && cc.t + 1 == cc.te) {
+      finish(first);
+      reset();
+      first = false;
+      if (cc.x + 1 >= hi) {
+        cc.x = hi;
+      } else {
+        advance(cc);
+        read_q(cc.a1 - cc.a0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // q_lds read before the next prefetch lands
+        if (live) stage_s(set_ptr(std::integral_constant<int, 0>{}), Sb[0]);
+        entered = true;
+      }
+    }
+    int i2, hk2;
+    if (entered && next_seg(i2, hk2))
+      prefetch_q(i2, hk2);
+    else
+      prefetch_none();
+  };
+
+  // prologue: Q of the first segment and tiles 0..2 in flight; then Q in
+  // registers, S^T of tile 0, the next segment's Q prefetched
+  prefetch_q(cc.i, cc.hk);
+  issue(std::integral_constant<int, 0>{});
+  advance(ic);
+  issue(std::integral_constant<int, 1>{});
+  advance(ic);
+  issue(std::integral_constant<int, 2>{});
+  advance(ic);
+  wait_vm<(NR - 2) * DPR, true>();
+  ring_barrier();
+  read_q(cc.a1 - cc.a0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (live) stage_s(ring0, Sb[0]);
+  {
+    int i2, hk2;
+    if (next_seg(i2, hk2))
+      prefetch_q(i2, hk2);
+    else
+      prefetch_none();
+  }
+  for (long long x = lo; x < hi; x += NR) {
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    boundary();
+  }
+  wait_vm<0, true>();
+}
+
+// Merge the parts of every cut segment written by attn_gqa_stream_kernel in
+// the launch before: workgroup (sequence i, KV head hk) recomputes the
+// partition, returns at once when its segment was not cut, and otherwise
+// wave wid merges query head hk * g + wid over the segment's parts in
+// workgroup order.  Lane (row, half) merges head-dim columns 64 half + 32
+// pass + [0, 32) of query row `row` in two passes; within a pass the parts
+// go in groups of four whose loads are all issued before any is used, and
+// the running (M, L, O) is rescaled group by group.
+__global__ __launch_bounds__(kGqaThreads) void attn_stream_merge_kernel(AttnArgs a) {
+  const int i = blockIdx.x / a.Hkv, hk = blockIdx.x % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wid >= a.g) return;
+  const int b = a.sq.b;
+  long long total = 0, before = 0;
+  for (int i0 = 0; i0 < b; i0 += 64) {
+    const int n = i0 + lane < b ? seq_tiles(a, i0 + lane) : 0;
+    total += __shfl(wave_scan_incl(n), 63, 64);
+    const int nb = i0 + lane < i ? n : 0;
+    before += __shfl(wave_scan_incl(nb), 63, 64);
+  }
+  const long long T = uniform_ll(total * a.Hkv);
+  const long long TQ = T / kStreamQuad;
+  const int Gn = (int)((long long)kNumCUs < TQ ? (long long)kNumCUs : TQ);
+  const int n_i = seq_tiles(a, i);
+  const long long seg0 = uniform_ll(before * a.Hkv + (long long)hk * n_i);
+  const int u0 = stream_owner(seg0, T, Gn), u1 = stream_owner(seg0 + n_i - 1, T, Gn);
+  if (u0 == u1) return;  // written whole by its workgroup
+  const int P = seq_prompt(a.sq, i);
+  int a0, a1;
+  fresh_range(a.mode, P, a.sq.G, a.sq.B, seq_block(a.sq, i), a0, a1);
+  const int nq = a1 - a0;
+  const int h = hk * a.g + wid;
+  const float c = a.scale_log2;
+  const int row = lane & 31, half = lane >> 5;
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    float M = -INFINITY, Lsum = 0.f;
+    float acc[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acc[k] = 0.f;
+    const int col0 = 64 * half + 32 * pass;
+#pragma unroll 1
+    for (int ub = u0; ub <= u1; ub += 4) {
+      float4 x[4][4];
+      float mp[4], lp[4], sp[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int u = min(ub + e, u1);  // past the last part: re-read it (weight 0 below)
+        const int slot = (u == u0 && stream_lo(u, T, Gn) < seg0) ? 1 : 0;
+        const uint8_t* part = (const uint8_t*)a.part + ((size_t)(2 * u + slot) * kGqaWaves + wid) * kPart16Bytes;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[e][v] = *(const float4*)(part + row * 256 + 2 * col0 + 16 * v);
+        const float* hdr = (const float*)(part + kQT * kD * 2);
+        mp[e] = hdr[row];
+        lp[e] = hdr[kQT + row];
+        sp[e] = hdr[2 * kQT + row];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ub + e > u1) mp[e] = -INFINITY;  // a re-read part adds nothing
+      float Mn = M;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Mn = fmaxf(Mn, mp[e]);
+      const float fo = exp2_fast((M - Mn) * c);
+      Lsum *= fo;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) acc[k] *= fo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float fn = exp2_fast((mp[e] - Mn) * c);
+        Lsum = fmaf(lp[e], fn, Lsum);
+        const float ws = fn * sp[e];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t wv[4] = {__float_as_uint(x[e][v].x), __float_as_uint(x[e][v].y), __float_as_uint(x[e][v].z),
+                                  __float_as_uint(x[e][v].w)};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float lo2, hi2;
+            unpack_f16x2(wv[k], lo2, hi2);
+            acc[8 * v + 2 * k] = fmaf(lo2, ws, acc[8 * v + 2 * k]);
+            acc[8 * v + 2 * k + 1] = fmaf(hi2, ws, acc[8 * v + 2 * k + 1]);
+          }
+        }
+      }
+      M = Mn;
+    }
+    if (row < nq) {
+      const float inv = 1.f / Lsum;
+      uint16_t* orow = (uint16_t*)a.out + (((size_t)i * a.fresh_rows + row) * a.Hq + h) * kD + col0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        uint4 u;
+        u.x = pack_bf16x2(acc[8 * v + 0] * inv, acc[8 * v + 1] * inv);
+        u.y = pack_bf16x2(acc[8 * v + 2] * inv, acc[8 * v + 3] * inv);
+        u.z = pack_bf16x2(acc[8 * v + 4] * inv, acc[8 * v + 5] * inv);
+        u.w = pack_bf16x2(acc[8 * v + 6] * inv, acc[8 * v + 7] * inv);
+        *(uint4*)(orow + 8 * v) = u;
+      }
+    }
   }
 }
 
@@ -1459,8 +2084,8 @@ static long attn_env_target() {
 // Kernel and work split (see the choice of QT below).  The key split fills
 // the GPU when there are few work items.  The environment
 // variables FDLLM_ATTN_QT (1: split-key kernel, 2, 4: LDS ring, 8: LDS ring
-// with 8 waves of one query tile each) and FDLLM_ATTN_TARGET_WGS override
-// the defaults for tuning.
+// with 8 waves of one query tile each, 16: that ring over the batch's tile
+// stream) and FDLLM_ATTN_TARGET_WGS override the defaults for tuning.
 AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max) {
   AttnPlan p{};
   if (dtype != 0 || d != kD) {  // vector-ALU kernel: four query rows per workgroup
@@ -1484,8 +2109,21 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   // A GQA group of 4 or more heads with one query tile each: the 8-wave
   // ring (8 query tiles per workgroup), so the group's heads share every K/V
   // tile.
-  if (QT != 1 && QT != 2 && QT != 4 && QT != 8) QT = p.n_qt == 1 ? (g >= 4 ? 8 : 1) : (T >= 4 ? 4 : 2);
+  if (QT != 1 && QT != 2 && QT != 4 && QT != 8 && QT != 16) QT = p.n_qt == 1 ? (g >= 4 ? 8 : 1) : (T >= 4 ? 4 : 2);
+  if (QT == 16 && !(p.n_qt == 1 && g <= kGqaWaves)) QT = 8;  // the tile stream needs one query tile per wave
   p.qt_per_wg = QT;
+  if (QT == 16) {
+    // 8-wave ring over the batch's tile stream: one persistent workgroup per
+    // CU, two partial slots of 8 query tiles each per workgroup
+    p.n_grp = 1;
+    p.n_split = 1;
+    p.kchunk = L_max;
+    p.grid = kNumCUs;
+    p.n_items = p.grid;
+    p.per_xcd = p.grid / 8;
+    p.part_bytes = (size_t)p.grid * 2 * kGqaWaves * kPart16Bytes;
+    return p;
+  }
   long base;
   int unit;
   if (QT == 1) {  // split-key kernel: one item per (sequence, query head, query tile, key chunk)
@@ -1575,6 +2213,13 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, in
   const LaunchEvents ev = take_launch_events();
   if (dtype == 0 && d == kD) {
     const dim3 grid((unsigned)p.grid), block(kThreads);
+    if (p.qt_per_wg == 16) {
+      const hipError_t e =
+          launch_kernel(attn_gqa_stream_kernel<4>, grid, dim3(kGqaThreads), 0, st, ev.start, (hipEvent_t) nullptr, a);
+      if (e != hipSuccess) return e;
+      return launch_kernel(attn_stream_merge_kernel, dim3((unsigned)(a.sq.b * a.Hkv)), dim3(kGqaThreads), 0, st,
+                           (hipEvent_t) nullptr, ev.stop, a);
+    }
     if (p.qt_per_wg == 8) {
       auto* kern = attn_gqa_kernel<4>;
       const dim3 gblock(kGqaThreads);

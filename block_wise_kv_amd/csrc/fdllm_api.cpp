@@ -325,8 +325,8 @@ LaunchEvents take_launch_events() {
 extern "C" {
 
 fdllm_status fdllm_set_tuning(int32_t attn_qt, int32_t attn_wgs, int32_t unmask_wgs) {
-  if (attn_qt != 0 && attn_qt != 1 && attn_qt != 2 && attn_qt != 4 && attn_qt != 8)
-    return fail(FDLLM_ERR_INVALID_ARG, "attn_qt must be 0, 1, 2, 4 or 8 (got %d)", attn_qt);
+  if (attn_qt != 0 && attn_qt != 1 && attn_qt != 2 && attn_qt != 4 && attn_qt != 8 && attn_qt != 16)
+    return fail(FDLLM_ERR_INVALID_ARG, "attn_qt must be 0, 1, 2, 4, 8 or 16 (got %d)", attn_qt);
   if (attn_wgs < 0 || unmask_wgs < 0 || attn_wgs > 65536 || unmask_wgs > 65536)
     return fail(FDLLM_ERR_INVALID_ARG, "workgroup targets must be in [0, 65536]");
   set_attn_tuning(attn_qt, attn_wgs);

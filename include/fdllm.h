@@ -343,14 +343,19 @@ fdllm_status fdllm_set_timing_events(void* start_event, void* stop_event);
  *               workgroup, bf16); 2 or 4: LDS-ring kernel with that many
  *               query tiles of one KV head per workgroup; 8: 8-wave LDS ring
  *               with one query tile per wave (8 per workgroup), key-chunk
- *               partials merged by a second kernel in the same call.
+ *               partials merged by a second kernel in the same call; 16:
+ *               the 8-wave ring run over the whole batch's K/V tile stream,
+ *               cut into equal ranges, one persistent workgroup per CU, the
+ *               pieces of cut (sequence, KV head) segments merged by a
+ *               second kernel (one query tile per head and at most 8 heads
+ *               per KV head; other geometries take 8).
  *   attn_wgs    workgroups the attention key split aims for (0..65536).
  *   unmask_wgs  workgroups the unmask vocab split aims for (0..65536).
  * Per host thread: they apply to the calls and workspace queries made on
  * the calling thread only.  The workspace sizes reported afterwards follow
  * the new plan: query them again and re-zero a workspace sized under the
  * old setting before reusing it (calls check the size they need).
- * FDLLM_ERR_INVALID_ARG for an attn_qt outside {0, 1, 2, 4, 8} or a target
+ * FDLLM_ERR_INVALID_ARG for an attn_qt outside {0, 1, 2, 4, 8, 16} or a target
  * outside [0, 65536]. */
 fdllm_status fdllm_set_tuning(int32_t attn_qt, int32_t attn_wgs, int32_t unmask_wgs);
 

@@ -95,17 +95,24 @@ def test_c4_large_batch(B):
     check_attn(out, _full(inp), inp, label=f"c4 B={B}")
 
 
-def test_c5_ragged():
-    # all 64 ragged sequences (prompts 256..4096, block index 0..15)
+@pytest.mark.parametrize("qt", [0, 8, 16])
+def test_c5_ragged(qt):
+    # all 64 ragged sequences (prompts 256..4096, block index 0..15), with
+    # the planner's kernel and the two 8-wave rings
+    import block_wise_kv_amd as fd
     s = shape_c5()
     inp = make_attn_inputs(s, "dual")
-    say("c5 ragged")
-    out, outs, _ = run_attn(inp, ragged=True, reps=2)
-    check_attn(out, _full(inp), inp, label="c5")
+    say(f"c5 ragged qt={qt}")
+    fd.set_tuning(attn_qt=qt)
+    try:
+        out, outs, _ = run_attn(inp, ragged=True, reps=2)
+    finally:
+        fd.set_tuning()
+    check_attn(out, _full(inp), inp, label=f"c5 qt={qt}")
     assert np.array_equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("qt", [0, 1, 2, 4, 8])
+@pytest.mark.parametrize("qt", [0, 1, 2, 4, 8, 16])
 def test_prefix_workspace_reused_over_block_indices(qt):
     # One workspace, zeroed once, serves a whole prefix-mode decode loop on
     # the LLaDA-8B shape: the query rows shrink from 256 to 32 as the block
@@ -196,7 +203,7 @@ def _dominant_key_case(mode):
 
 @pytest.mark.parametrize("mode", ["dual", "prefix", "none"])
 @pytest.mark.parametrize("wgs", [0, 16, 4096])
-@pytest.mark.parametrize("qt", [1, 2, 4, 8])
+@pytest.mark.parametrize("qt", [1, 2, 4, 8, 16])
 def test_dominant_key_at_boundaries(qt, wgs, mode):
     # every kernel variant and key split: each query row must return the V
     # row of its planted key, at every tile / chunk edge and fresh-range edge
@@ -266,11 +273,12 @@ VARIANTS = [
 
 
 @pytest.mark.parametrize("wgs", [0, 16, 4096])
-@pytest.mark.parametrize("qt", [1, 2, 4, 8])
+@pytest.mark.parametrize("qt", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("case", VARIANTS, ids=lambda c: c[0])
 def test_kernel_variants(case, qt, wgs):
     # every attention kernel (split-key, LDS ring with 2 or 4 query tiles per
-    # workgroup, 8-wave LDS ring with one per wave) and key split on the same inputs
+    # workgroup, 8-wave LDS ring with one per wave, the 8-wave ring over the
+    # batch's tile stream) and key split on the same inputs
     import block_wise_kv_amd as fd
     name, dt, b, hq, hkv, d, P, G, B, k, mode = case
     s = shape_custom(name, dt, b, hq, hkv, d, P, G, B, k, 64, cfg_id=52)
@@ -286,7 +294,7 @@ def test_kernel_variants(case, qt, wgs):
     assert np.array_equal(outs[0], outs[1], equal_nan=True)
 
 
-@pytest.mark.parametrize("qt", [1, 2, 4, 8])
+@pytest.mark.parametrize("qt", [1, 2, 4, 8, 16])
 def test_output_scales_exactly_with_v(qt):
     # Attention is linear in V, and scaling V by 2^e scales every product,
     # sum and stored partial by 2^e exactly (the 8-wave ring stores its split
