@@ -852,7 +852,7 @@ def c5_main(args):
         e.append(events.elapsed_s(2 * m, 2 * m + 1))
     events.close()
     copy_bps = large_copy_rate()
-    flops_attn = 4 * b * Hq * B * int(L.sum()) * d
+    flops_attn = 4 * Hq * B * int(L.sum()) * d  # S and P V: 2 B L d each per query head, L summed over the batch
     nbytes = {"block_attn": attn_bytes, "unmask_threshold": unm_bytes, "kv_refresh": ref_bytes}
     kernels = {}
     for name, ts in per.items():

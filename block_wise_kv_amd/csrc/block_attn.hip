@@ -620,6 +620,54 @@ __device__ __forceinline__ float pairwise_sum16(const float* x) {
   return (t[0] + t[2]) + (t[1] + t[3]);
 }
 
+// Online-softmax step of one 32-key tile for the 8-wave kernels, with the
+// tile's scores S^T in the MFMA accumulator layout (lane (lq, hh): query
+// column lq, 16 keys).  The weights p = 2^(c (S - m_ref)) are taken against
+// the running reference m_ref first; only when a column's 16 weights sum
+// past 2^kSumCap, or are not finite (the first tile, whose reference is
+// -inf), is the reference raised to the column maximum (over both lane
+// halves), O and l rescaled and p recomputed.  Exact in either branch: the
+// reference only scales the weights, and every weight stays <= 2^kSumCap.
+// l_run gains the weights' sum; pop gets them as bf16, the B operand of the
+// P V product.
+constexpr float kSumCap = 12.f;
+__device__ __forceinline__ void softmax_tile(f32x16& S, float c, float& m_ref, float& l_run, f32x16* O,
+                                             bf16x8* pop) {
+  const float mc = m_ref * c;
+  float p[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) p[r] = exp2_fast(fmaf(S[r], c, -mc));
+  float sum = pairwise_sum16(p);
+  if (__builtin_expect(__ballot(!(sum <= (float)(1 << (int)kSumCap))) != 0, 0)) {
+    float mx = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+    mx = xor_combine<32>(mx, [](float x, float y) { return fmaxf(x, y); });
+    const float m_new = fmaxf(m_ref, mx);
+    const float alpha = exp2_fast((m_ref - m_new) * c);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
+    m_ref = m_new;
+    const float mc2 = m_ref * c;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = exp2_fast(fmaf(S[r], c, -mc2));
+    sum = pairwise_sum16(p);
+  }
+  l_run += sum;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    uint4 w;
+    w.x = cvt_pk_bf16(p[8 * h2 + 0], p[8 * h2 + 1]);
+    w.y = cvt_pk_bf16(p[8 * h2 + 2], p[8 * h2 + 3]);
+    w.z = cvt_pk_bf16(p[8 * h2 + 4], p[8 * h2 + 5]);
+    w.w = cvt_pk_bf16(p[8 * h2 + 6], p[8 * h2 + 7]);
+    pop[h2] = as_bf16x8(w);
+  }
+}
+
 // ------------------------------------------------------------------ bf16 MFMA, LDS ring
 template <int QT, int NR>
 __global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_ring_kernel(AttnArgs a) {
@@ -1121,6 +1169,10 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   const char* vf_row0 = (const char*)vnp + ((size_t)g.i * a.fresh_rows * a.Hkv + g.hk) * 256;
   auto issue = [&](int q, auto jc) __attribute__((always_inline)) {
     uint8_t* dst = set_ptr(jc) + wid * 1024;
+    // (hidden from alias analysis: the compiler otherwise takes the reads of
+    // the other ring sets in this round as depending on these loads and
+    // waits for all of them; the explicit waits order every hand-off)
+    asm volatile("" : "+s"(dst));
     const int t0 = g.kb + q * kKT;
     const bool whole = t0 + kKT <= g.ke;
     const bool in_cache = whole && (t0 + kKT <= g.a0 || t0 >= g.a1);
@@ -1198,35 +1250,8 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
         if (key >= g.ke) S[r] = -INFINITY;
       }
     }
-    float mx = S[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-    mx = xor_combine<32>(mx, [](float x, float y) { return fmaxf(x, y); });
-    if (__ballot((mx - m_ref) * c > kRefSlack)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = exp2_fast((m_ref - m_new) * c);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-      m_ref = m_new;
-    }
-    const float mc = m_ref * c;
-    float p[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = exp2_fast(fmaf(S[r], c, -mc));
-    l_run += pairwise_sum16(p);
     bf16x8 pop[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      uint4 w;
-      w.x = cvt_pk_bf16(p[8 * h2 + 0], p[8 * h2 + 1]);
-      w.y = cvt_pk_bf16(p[8 * h2 + 2], p[8 * h2 + 3]);
-      w.z = cvt_pk_bf16(p[8 * h2 + 4], p[8 * h2 + 5]);
-      w.w = cvt_pk_bf16(p[8 * h2 + 6], p[8 * h2 + 7]);
-      pop[h2] = as_bf16x8(w);
-    }
+    softmax_tile(S, c, m_ref, l_run, O, pop);
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
@@ -1424,10 +1449,11 @@ __device__ __forceinline__ int stream_owner(long long x, long long T, int G) {
 
 // A workgroup's place in its tile range: the segment (sequence i, KV head
 // hk), the tile t within it, this workgroup's part of the segment [tb, te),
-// the global tile index x, and the segment's geometry.  Wave-uniform.
+// the tiles of the range left from t on (0: past the range), and the
+// segment's geometry.  Wave-uniform.
 struct StreamCursor {
   int i, hk, t, tb, te, n;
-  long long x;
+  int left;
   int L, a0, a1, ke;
   const char *kc, *vc, *kf, *vf;  // row 0 of the segment's cached and fresh K / V
 };
@@ -1517,7 +1543,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
     fresh_range(mode, P, Gl, Bl, block_of(cu.i), cu.a0, cu.a1);
     cu.n = tiles_of_len(cu.L);
     cu.tb = cu.t;
-    cu.te = (int)min((long long)cu.n, (long long)cu.t + (hi - cu.x));
+    cu.te = min(cu.n, cu.t + cu.left);
     cu.ke = max(min(cu.L, cu.te * kKT), cu.tb * kKT + 1);  // at least one key row to clamp to
     const size_t cb = ((size_t)cu.i * Hkv + cu.hk) * Lcap * 256;
     const size_t fb = ((size_t)cu.i * fresh_rows * Hkv + cu.hk) * 256;
@@ -1529,11 +1555,11 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
   // one tile on: past the part's end the cursor enters the next segment
   // (while the range lasts; past it, it stays on its last tile)
   auto advance = [&](StreamCursor& cu) __attribute__((always_inline)) {
-    if (cu.x + 1 >= hi) {
-      cu.x = hi;
+    if (cu.left <= 1) {
+      cu.left = 0;
       return;
     }
-    ++cu.x;
+    --cu.left;
     if (++cu.t == cu.te) {
       cu.t = 0;
       if (++cu.hk == Hkv) {
@@ -1551,7 +1577,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
     ic.i = i_lo;
     ic.hk = (int)((lo - base) / n0);
     ic.t = (int)((lo - base) % n0);
-    ic.x = lo;
+    ic.left = (int)(hi - lo);
     enter(ic);
   }
   StreamCursor cc = ic;  // compute cursor
@@ -1566,13 +1592,13 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
   const size_t fstride = (size_t)Hkv * 256;
   const uint32_t off_c = (uint32_t)(row_a * 256 + 16 * chunk_a);
   const uint32_t off_f = (uint32_t)(row_a * Hkv * 256 + 16 * chunk_a);
-  auto issue = [&](auto jc) __attribute__((always_inline)) {
+  auto issue_tile = [&](auto jc, int tile) __attribute__((always_inline)) {
     uint8_t* dst = set_ptr(jc) + wid * 1024;
     // (hidden from alias analysis: the compiler otherwise takes the reads of
     // the other ring sets in this step as depending on these loads and waits
     // for all of them; the explicit waits above order every hand-off)
     asm volatile("" : "+s"(dst));
-    const int t0 = (ic.x < hi ? ic.t : ic.te - 1) * kKT;
+    const int t0 = tile * kKT;
     const bool whole = t0 + kKT <= ic.ke;
     const bool in_cache = whole && (t0 + kKT <= ic.a0 || t0 >= ic.a1);
     const bool in_fresh = whole && t0 >= ic.a0 && t0 + kKT <= ic.a1;
@@ -1589,6 +1615,9 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
       __builtin_amdgcn_global_load_lds(kt + 16 * chunk_a, dst, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vt + 16 * chunk_a, dst + kTileBytes, 16, 0, 0);
     }
+  };
+  auto issue = [&](auto jc) __attribute__((always_inline)) {
+    issue_tile(jc, ic.left > 0 ? ic.t : ic.te - 1);
   };
   // This wave's Q tile of the segment after the compute cursor's current one
   // (query head hk * g + wid of that segment) into its 8 KB of q_lds: row r
@@ -1610,14 +1639,14 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
       __builtin_amdgcn_global_load_lds((const char*)src + 16 * k, dst + v * 1024, 16, 0, 0);
     }
   };
-  // The same number of loads with nothing to fetch: every lane copies the
-  // first 16 bytes of Q into this wave's KB of q_sink.  Every quad of steps
-  // issues QLD Q-side loads per wave, a prefetch or these, so the count of
-  // loads in flight at each wait is the same on every path.
+  // The same number of loads with next to nothing to fetch: every lane
+  // copies the first byte of Q into this wave's part of q_sink.  Every quad
+  // of steps issues QLD Q-side loads per wave, a prefetch or these, so the
+  // count of loads in flight at each wait is the same on every path.
   auto prefetch_none = [&]() __attribute__((always_inline)) {
     uint8_t* dst = q_sink + wid * 1024;
 #pragma unroll
-    for (int v = 0; v < QLD; ++v) __builtin_amdgcn_global_load_lds((const char*)qp, dst, 16, 0, 0);
+    for (int v = 0; v < QLD; ++v) __builtin_amdgcn_global_load_lds((const char*)qp, dst, 1, 0, 0);
   };
   // Q as the B operand of S^T = K Q^T from q_lds: lane (lq, hh) holds query
   // row lq, columns [16 ks + 8 hh, +8) for ks = 0..7; rows past nq are zero
@@ -1692,35 +1721,8 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
         if (key >= ke) S[r] = -INFINITY;
       }
     }
-    float mx = S[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-    mx = xor_combine<32>(mx, [](float x, float y) { return fmaxf(x, y); });
-    if (__ballot((mx - m_ref) * c > kRefSlack)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = exp2_fast((m_ref - m_new) * c);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[dt][r] *= alpha;
-      m_ref = m_new;
-    }
-    const float mc = m_ref * c;
-    float p[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = exp2_fast(fmaf(S[r], c, -mc));
-    l_run += pairwise_sum16(p);
     bf16x8 pop[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      uint4 u;
-      u.x = cvt_pk_bf16(p[8 * h2 + 0], p[8 * h2 + 1]);
-      u.y = cvt_pk_bf16(p[8 * h2 + 2], p[8 * h2 + 3]);
-      u.z = cvt_pk_bf16(p[8 * h2 + 4], p[8 * h2 + 5]);
-      u.w = cvt_pk_bf16(p[8 * h2 + 6], p[8 * h2 + 7]);
-      pop[h2] = as_bf16x8(u);
-    }
+    softmax_tile(S, c, m_ref, l_run, O, pop);
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
@@ -1795,7 +1797,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
   bool first = true;  // the compute cursor is in this workgroup's first segment
   // the segment after the compute cursor's current one (if the range reaches it)
   auto next_seg = [&](int& i2, int& hk2) __attribute__((always_inline)) -> bool {
-    if (cc.x + (cc.te - cc.t) >= hi) return false;
+    if (cc.te - cc.t >= cc.left) return false;
     i2 = cc.i;
     hk2 = cc.hk + 1;
     if (hk2 == Hkv) {
@@ -1810,7 +1812,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
     ring_barrier();
     issue(std::integral_constant<int, (J + NR - 1) % NR>{});
     advance(ic);
-    if (cc.x >= hi) return;  // past the range: the loads above keep the counts exact
+    if (cc.left <= 0) return;  // past the range: the loads above keep the counts exact
     // segment parts are whole quads: tile x + 1 leaves the part only after
     // the quad's last step, which boundary() handles
     const bool more = J < NR - 1 || cc.t + 1 < cc.te;
@@ -1822,12 +1824,12 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
   };
   auto boundary = [&]() __attribute__((always_inline)) {
     bool entered = false;
-    if (cc.x < hi && cc.t + 1 == cc.te) {
+    if (cc.left > 0 && cc.t + 1 == cc.te) {
       finish(first);
       reset();
       first = false;
-      if (cc.x + 1 >= hi) {
-        cc.x = hi;
+      if (cc.left <= 1) {
+        cc.left = 0;
       } else {
         advance(cc);
         read_q(cc.a1 - cc.a0);
@@ -1864,7 +1866,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
     else
       prefetch_none();
   }
-  for (long long x = lo; x < hi; x += NR) {
+  for (int qd = (int)(hi - lo) / NR; qd > 0; --qd) {
     step(std::integral_constant<int, 0>{});
     step(std::integral_constant<int, 1>{});
     step(std::integral_constant<int, 2>{});
@@ -2086,7 +2088,7 @@ static long attn_env_target() {
 // variables FDLLM_ATTN_QT (1: split-key kernel, 2, 4: LDS ring, 8: LDS ring
 // with 8 waves of one query tile each, 16: that ring over the batch's tile
 // stream) and FDLLM_ATTN_TARGET_WGS override the defaults for tuning.
-AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max) {
+AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max, bool ragged) {
   AttnPlan p{};
   if (dtype != 0 || d != kD) {  // vector-ALU kernel: four query rows per workgroup
     p.n_qt = (nq_max + 3) / 4;
@@ -2108,8 +2110,13 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
   // (prefix / no cache): the ring, four query tiles per K/V tile.
   // A GQA group of 4 or more heads with one query tile each: the 8-wave
   // ring (8 query tiles per workgroup), so the group's heads share every K/V
-  // tile.
-  if (QT != 1 && QT != 2 && QT != 4 && QT != 8 && QT != 16) QT = p.n_qt == 1 ? (g >= 4 ? 8 : 1) : (T >= 4 ? 4 : 2);
+  // tile; with per-sequence prompt lengths and at least half as many
+  // (sequence, KV head) segments as CUs, that ring over the batch's tile
+  // stream, which gives every CU the same number of tiles (one workgroup
+  // per segment would last as long as the longest sequence).
+  if (QT != 1 && QT != 2 && QT != 4 && QT != 8 && QT != 16)
+    QT = p.n_qt == 1 ? (g >= 4 ? (ragged && g <= kGqaWaves && (long)b * Hkv >= kNumCUs / 2 ? 16 : 8) : 1)
+                     : (T >= 4 ? 4 : 2);
   if (QT == 16 && !(p.n_qt == 1 && g <= kGqaWaves)) QT = 8;  // the tile stream needs one query tile per wave
   p.qt_per_wg = QT;
   if (QT == 16) {
@@ -2182,14 +2189,14 @@ size_t attn_counter_bytes(int b, int Hq, int nq_bound) {
 // A plan has one key chunk (no partials) once its work items reach the
 // workgroup target, and every kernel's item count is at least
 // b * Hq * n_qt / 8, so the scan stops there.
-size_t attn_workspace_bytes(int dtype, int b, int Hq, int Hkv, int d, int nq_bound, int L_max) {
+size_t attn_workspace_bytes(int dtype, int b, int Hq, int Hkv, int d, int nq_bound, int L_max, bool ragged) {
   if (dtype != 0 || d != kD) return 0;
   const long target_env = attn_env_target();
   const long tmax = g_attn_wgs > 0 ? g_attn_wgs : target_env > 0 ? target_env : 512;
   const int nqt_bound = (nq_bound + kQT - 1) / kQT;
   size_t part = 0;
   for (int t = 1; t <= nqt_bound; ++t) {
-    const AttnPlan p = plan_block_attn(dtype, b, Hq, Hkv, d, t < nqt_bound ? t * kQT : nq_bound, L_max);
+    const AttnPlan p = plan_block_attn(dtype, b, Hq, Hkv, d, t < nqt_bound ? t * kQT : nq_bound, L_max, ragged);
     if (p.part_bytes > part) part = p.part_bytes;
     if ((long)b * Hq * t >= 8 * tmax) break;
   }

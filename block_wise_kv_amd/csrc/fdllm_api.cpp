@@ -179,11 +179,13 @@ fdllm_status setup_attn(const fdllm_seq_desc* seq, const fdllm_attn_desc* ad, in
     return fail(FDLLM_ERR_INVALID_ARG, "tensor too large");
   if ((int64_t)seq->batch * ad->n_q_heads * ((need + 31) / 32) * ((su.L_max + 127) / 128) >= ((int64_t)1 << 31))
     return fail(FDLLM_ERR_INVALID_ARG, "grid too large");
-  su.plan = plan_block_attn(ad->dtype, seq->batch, ad->n_q_heads, ad->n_kv_heads, ad->head_dim, need, su.L_max);
+  const bool ragged_lens = seq->prompt_lens != nullptr;
+  su.plan = plan_block_attn(ad->dtype, seq->batch, ad->n_q_heads, ad->n_kv_heads, ad->head_dim, need, su.L_max,
+                            ragged_lens);
   su.counter_bytes = attn_counter_bytes(seq->batch, ad->n_q_heads, su.nq_bound);
   su.ws_call = su.plan.part_bytes > 0 ? su.counter_bytes + su.plan.part_bytes : 0;
   su.ws_geometry = attn_workspace_bytes(ad->dtype, seq->batch, ad->n_q_heads, ad->n_kv_heads, ad->head_dim,
-                                        su.nq_bound, su.L_max);
+                                        su.nq_bound, su.L_max, ragged_lens);
   return FDLLM_OK;
 }
 

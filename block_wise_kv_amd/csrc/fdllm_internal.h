@@ -160,10 +160,10 @@ struct AttnPlan {
   int n_qt, n_grp, n_split, kchunk, n_items, per_xcd, grid;
   size_t part_bytes;        // split partials (after the counters); 0: one key chunk, no workspace
 };
-AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max);
+AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, int L_max, bool ragged);
 void set_attn_tuning(int qt, int wgs);
 size_t attn_counter_bytes(int b, int Hq, int nq_bound);
-size_t attn_workspace_bytes(int dtype, int b, int Hq, int Hkv, int d, int nq_bound, int L_max);
+size_t attn_workspace_bytes(int dtype, int b, int Hq, int Hkv, int d, int nq_bound, int L_max, bool ragged);
 void attn_bind_workspace(AttnArgs& a, const AttnPlan& p, void* workspace, size_t counter_bytes);
 hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, int d, hipStream_t st);
 
