@@ -1880,10 +1880,10 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
 // the launch before: workgroup (sequence i, KV head hk) recomputes the
 // partition, returns at once when its segment was not cut, and otherwise
 // wave wid merges query head hk * g + wid over the segment's parts in
-// workgroup order.  Lane (row, half) merges head-dim columns 64 half + 32
-// pass + [0, 32) of query row `row` in two passes; within a pass the parts
-// go in groups of four whose loads are all issued before any is used, and
-// the running (M, L, O) is rescaled group by group.
+// workgroup order.  Lane (row, half) merges head-dim columns 64 half +
+// [0, 64) of query row `row`; the parts go in pairs whose loads are all
+// issued before any is used (a segment cut once is one memory round trip),
+// and the running (M, L, O) is rescaled pair by pair.
 __global__ __launch_bounds__(kGqaThreads) void attn_stream_merge_kernel(AttnArgs a) {
   const int i = blockIdx.x / a.Hkv, hk = blockIdx.x % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1911,71 +1911,64 @@ __global__ __launch_bounds__(kGqaThreads) void attn_stream_merge_kernel(AttnArgs
   const int h = hk * a.g + wid;
   const float c = a.scale_log2;
   const int row = lane & 31, half = lane >> 5;
+  float M = -INFINITY, Lsum = 0.f;
+  float acc[64];
+#pragma unroll
+  for (int k = 0; k < 64; ++k) acc[k] = 0.f;
+  const int col0 = 64 * half;
 #pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    float M = -INFINITY, Lsum = 0.f;
-    float acc[32];
+  for (int ub = u0; ub <= u1; ub += 2) {
+    float4 x[2][8];
+    float mp[2], lp[2], sp[2];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) acc[k] = 0.f;
-    const int col0 = 64 * half + 32 * pass;
-#pragma unroll 1
-    for (int ub = u0; ub <= u1; ub += 4) {
-      float4 x[4][4];
-      float mp[4], lp[4], sp[4];
+    for (int e = 0; e < 2; ++e) {
+      const int u = min(ub + e, u1);  // past the last part: re-read it (weight 0 below)
+      const int slot = (u == u0 && stream_lo(u, T, Gn) < seg0) ? 1 : 0;
+      const uint8_t* part = (const uint8_t*)a.part + ((size_t)(2 * u + slot) * kGqaWaves + wid) * kPart16Bytes;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int u = min(ub + e, u1);  // past the last part: re-read it (weight 0 below)
-        const int slot = (u == u0 && stream_lo(u, T, Gn) < seg0) ? 1 : 0;
-        const uint8_t* part = (const uint8_t*)a.part + ((size_t)(2 * u + slot) * kGqaWaves + wid) * kPart16Bytes;
+      for (int v = 0; v < 8; ++v) x[e][v] = *(const float4*)(part + row * 256 + 2 * col0 + 16 * v);
+      const float* hdr = (const float*)(part + kQT * kD * 2);
+      mp[e] = hdr[row];
+      lp[e] = hdr[kQT + row];
+      sp[e] = hdr[2 * kQT + row];
+    }
+    if (ub + 1 > u1) mp[1] = -INFINITY;  // a re-read part adds nothing
+    const float Mn = fmaxf(M, fmaxf(mp[0], mp[1]));
+    const float fo = exp2_fast((M - Mn) * c);
+    Lsum *= fo;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) x[e][v] = *(const float4*)(part + row * 256 + 2 * col0 + 16 * v);
-        const float* hdr = (const float*)(part + kQT * kD * 2);
-        mp[e] = hdr[row];
-        lp[e] = hdr[kQT + row];
-        sp[e] = hdr[2 * kQT + row];
-      }
+    for (int k = 0; k < 64; ++k) acc[k] *= fo;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (ub + e > u1) mp[e] = -INFINITY;  // a re-read part adds nothing
-      float Mn = M;
+    for (int e = 0; e < 2; ++e) {
+      const float fn = exp2_fast((mp[e] - Mn) * c);
+      Lsum = fmaf(lp[e], fn, Lsum);
+      const float ws = fn * sp[e];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Mn = fmaxf(Mn, mp[e]);
-      const float fo = exp2_fast((M - Mn) * c);
-      Lsum *= fo;
+      for (int v = 0; v < 8; ++v) {
+        const uint32_t wv[4] = {__float_as_uint(x[e][v].x), __float_as_uint(x[e][v].y), __float_as_uint(x[e][v].z),
+                                __float_as_uint(x[e][v].w)};
 #pragma unroll
-      for (int k = 0; k < 32; ++k) acc[k] *= fo;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float fn = exp2_fast((mp[e] - Mn) * c);
-        Lsum = fmaf(lp[e], fn, Lsum);
-        const float ws = fn * sp[e];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint32_t wv[4] = {__float_as_uint(x[e][v].x), __float_as_uint(x[e][v].y), __float_as_uint(x[e][v].z),
-                                  __float_as_uint(x[e][v].w)};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            float lo2, hi2;
-            unpack_f16x2(wv[k], lo2, hi2);
-            acc[8 * v + 2 * k] = fmaf(lo2, ws, acc[8 * v + 2 * k]);
-            acc[8 * v + 2 * k + 1] = fmaf(hi2, ws, acc[8 * v + 2 * k + 1]);
-          }
+        for (int k = 0; k < 4; ++k) {
+          float lo2, hi2;
+          unpack_f16x2(wv[k], lo2, hi2);
+          acc[8 * v + 2 * k] = fmaf(lo2, ws, acc[8 * v + 2 * k]);
+          acc[8 * v + 2 * k + 1] = fmaf(hi2, ws, acc[8 * v + 2 * k + 1]);
         }
       }
-      M = Mn;
     }
-    if (row < nq) {
-      const float inv = 1.f / Lsum;
-      uint16_t* orow = (uint16_t*)a.out + (((size_t)i * a.fresh_rows + row) * a.Hq + h) * kD + col0;
+    M = Mn;
+  }
+  if (row < nq) {
+    const float inv = 1.f / Lsum;
+    uint16_t* orow = (uint16_t*)a.out + (((size_t)i * a.fresh_rows + row) * a.Hq + h) * kD + col0;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        uint4 u;
-        u.x = pack_bf16x2(acc[8 * v + 0] * inv, acc[8 * v + 1] * inv);
-        u.y = pack_bf16x2(acc[8 * v + 2] * inv, acc[8 * v + 3] * inv);
-        u.z = pack_bf16x2(acc[8 * v + 4] * inv, acc[8 * v + 5] * inv);
-        u.w = pack_bf16x2(acc[8 * v + 6] * inv, acc[8 * v + 7] * inv);
-        *(uint4*)(orow + 8 * v) = u;
-      }
+    for (int v = 0; v < 8; ++v) {
+      uint4 u;
+      u.x = pack_bf16x2(acc[8 * v + 0] * inv, acc[8 * v + 1] * inv);
+      u.y = pack_bf16x2(acc[8 * v + 2] * inv, acc[8 * v + 3] * inv);
+      u.z = pack_bf16x2(acc[8 * v + 4] * inv, acc[8 * v + 5] * inv);
+      u.w = pack_bf16x2(acc[8 * v + 6] * inv, acc[8 * v + 7] * inv);
+      *(uint4*)(orow + 8 * v) = u;
     }
   }
 }
