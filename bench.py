@@ -326,12 +326,23 @@ def cpu_baseline(seconds: float):
                       f"in {el:.1f} s, fp64 NumPy oracle, BLAS limited to 1 thread"}
 
 
-def kernel_source_sha256() -> str:
-    """Digest of the HIP sources the counters were taken on (all of csrc/)."""
+# The sources each reported kernel is built from (besides the shared device
+# and internal headers): counters taken on them stay valid until one changes.
+KERNEL_SOURCES = {
+    "block_attn": ["block_attn.hip"],
+    "unmask_threshold": ["unmask.hip"],
+    "kv_refresh": ["kv_refresh.hip"],
+    "lmhead_unmask": ["lmhead.hip", "unmask.hip"],
+}
+SHARED_SOURCES = ["fdllm_device.h", "fdllm_internal.h"]
+
+
+def kernel_source_sha256(kernel: str) -> str:
+    """Digest of the HIP sources `kernel` is built from."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_wise_kv_amd", "csrc")
-    for name in sorted(os.listdir(d)):
+    for name in sorted(KERNEL_SOURCES[kernel] + SHARED_SOURCES):
         with open(os.path.join(d, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -341,7 +352,7 @@ def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, scaled by what they read for a plain
     copy of known size); None when there is no summary for this workload or
-    the kernels have changed since the counters were taken."""
+    the kernel's sources have changed since the counters were taken."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic.md")
     try:
         text = open(path).read()
@@ -355,7 +366,8 @@ def measured_traffic(workload: str, kernel: str):
         data = json.loads(text[start + 7:end])
     except ValueError:
         return None
-    if data.get("source_sha256") != kernel_source_sha256():
+    shas = data.get("source_sha256")
+    if kernel not in KERNEL_SOURCES or not isinstance(shas, dict) or shas.get(kernel) != kernel_source_sha256(kernel):
         return None
     k = data.get("workloads", {}).get(workload, {}).get(kernel)
     if not k:

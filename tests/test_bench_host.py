@@ -33,14 +33,15 @@ def _summary():
 def test_traffic_summary_is_read_as_written():
     b = _bench()
     data = _summary()
-    assert re.fullmatch(r"[0-9a-f]{64}", data["source_sha256"])
-    for w in ("c2", "c3", "c4"):
+    for k, sha in data["source_sha256"].items():
+        assert k in b.KERNEL_SOURCES and re.fullmatch(r"[0-9a-f]{64}", sha)
+    for w in ("c2", "c3", "c4", "c5"):
         for k in ("block_attn", "unmask_threshold", "kv_refresh"):
             e = data["workloads"][w][k]
             want = int(round(e["fetch_kib"] * 1024 * data["fetch_scale"] + e["write_kib"] * 1024 * data["write_scale"]))
             got = b.measured_traffic(w, k)
             # the counters apply only to the sources they were taken on
-            if data["source_sha256"] == b.kernel_source_sha256():
+            if data["source_sha256"][k] == b.kernel_source_sha256(k):
                 assert got == want
             else:
                 assert got is None
