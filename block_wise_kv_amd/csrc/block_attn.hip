@@ -1455,7 +1455,8 @@ struct StreamCursor {
   int i, hk, t, tb, te, n;
   int left;
   int L, a0, a1, ke;
-  const char *kc, *vc, *kf, *vf;  // row 0 of the segment's cached and fresh K / V
+  const char *kc, *kf;  // row 0 of the segment's cached and fresh K
+  long long dvc, dvf;   // V minus K: the same rows of the cached and fresh V
 };
 
 template <int NR>
@@ -1464,10 +1465,12 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
   constexpr int DPR = 2;   // ring loads per wave per tile
   constexpr int QLD = 8;   // Q-prefetch loads per wave (32 rows x 256 bytes)
   static_assert(NR == 4, "four ring sets");
-  __shared__ __attribute__((aligned(16))) uint8_t ring0[SET];
-  __shared__ __attribute__((aligned(16))) uint8_t ring1[SET];
-  __shared__ __attribute__((aligned(16))) uint8_t ring2[SET];
-  __shared__ __attribute__((aligned(16))) uint8_t ring3[SET];
+  // (the ring sets' larger alignment places them first, in the low 64 KB of
+  // LDS, where their base fits a read's immediate offset)
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[SET];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[SET];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[SET];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[SET];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kGqaWaves * kQT * 256];  // each wave's next Q tile
   __shared__ __attribute__((aligned(16))) uint8_t q_sink[kGqaWaves * 1024];      // never read (see prefetch_none)
   auto set_ptr = [&](auto jc) __attribute__((always_inline)) -> uint8_t* {
@@ -1548,9 +1551,9 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
     const size_t cb = ((size_t)cu.i * Hkv + cu.hk) * Lcap * 256;
     const size_t fb = ((size_t)cu.i * fresh_rows * Hkv + cu.hk) * 256;
     cu.kc = (const char*)a.kc + cb;
-    cu.vc = (const char*)a.vc + cb;
     cu.kf = (const char*)a.kn + fb;
-    cu.vf = (const char*)a.vn + fb;
+    cu.dvc = (const char*)a.vc - (const char*)a.kc;
+    cu.dvf = (const char*)a.vn - (const char*)a.kn;
   };
   // one tile on: past the part's end the cursor enters the next segment
   // (while the range lasts; past it, it stays on its last tile)
@@ -1592,28 +1595,35 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
   const size_t fstride = (size_t)Hkv * 256;
   const uint32_t off_c = (uint32_t)(row_a * 256 + 16 * chunk_a);
   const uint32_t off_f = (uint32_t)(row_a * Hkv * 256 + 16 * chunk_a);
+  typedef __attribute__((address_space(3))) void* LdsV;
   auto issue_tile = [&](auto jc, int tile) __attribute__((always_inline)) {
-    uint8_t* dst = set_ptr(jc) + wid * 1024;
-    // (hidden from alias analysis: the compiler otherwise takes the reads of
-    // the other ring sets in this step as depending on these loads and waits
-    // for all of them; the explicit waits above order every hand-off)
+    // The destination as a plain LDS address, hidden from alias analysis:
+    // the compiler otherwise takes the reads of the other ring sets in this
+    // step as depending on these loads and waits for all of them (the
+    // explicit waits above order every hand-off)
+    uint32_t dst = lds_addr(set_ptr(jc)) + wid * 1024;
     asm volatile("" : "+s"(dst));
+    const LdsV dk = (LdsV)(uintptr_t)dst, dv = (LdsV)(uintptr_t)(dst + kTileBytes);
     const int t0 = tile * kKT;
+    // (branch-free tests: a whole tile is in the cache unless it overlaps
+    // [a0, a1), and in the fresh rows if it lies inside [a0, a1))
     const bool whole = t0 + kKT <= ic.ke;
-    const bool in_cache = whole && (t0 + kKT <= ic.a0 || t0 >= ic.a1);
-    const bool in_fresh = whole && t0 >= ic.a0 && t0 + kKT <= ic.a1;
-    if (in_cache || in_fresh) {
-      const char* kt = in_cache ? ic.kc + (size_t)t0 * 256 + off_c : ic.kf + (size_t)(t0 - ic.a0) * fstride + off_f;
-      const char* vt = in_cache ? ic.vc + (size_t)t0 * 256 + off_c : ic.vf + (size_t)(t0 - ic.a0) * fstride + off_f;
-      __builtin_amdgcn_global_load_lds(kt, dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vt, dst + kTileBytes, 16, 0, 0);
+    const bool overlaps = (unsigned)(t0 - (ic.a0 - kKT + 1)) < (unsigned)(ic.a1 - ic.a0 + kKT - 1);
+    const bool inside = (ic.a1 - ic.a0 >= kKT) & ((unsigned)(t0 - ic.a0) <= (unsigned)(ic.a1 - ic.a0 - kKT));
+    const bool in_cache = whole & !overlaps;
+    if (whole & (!overlaps | inside)) {
+      const char* kt = in_cache ? ic.kc + ((size_t)(uint32_t)t0 << 8) : ic.kf + (size_t)(uint32_t)(t0 - ic.a0) * fstride;
+      const char* vt = kt + (in_cache ? ic.dvc : ic.dvf);
+      const uint32_t off = in_cache ? off_c : off_f;
+      __builtin_amdgcn_global_load_lds(kt + off, dk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vt + off, dv, 16, 0, 0);
     } else {
       const int j = min(t0 + row_a, ic.ke - 1);
       const bool fr = (unsigned)(j - ic.a0) < (unsigned)(ic.a1 - ic.a0);
-      const char* kt = fr ? ic.kf + (size_t)(j - ic.a0) * fstride : ic.kc + (size_t)j * 256;
-      const char* vt = fr ? ic.vf + (size_t)(j - ic.a0) * fstride : ic.vc + (size_t)j * 256;
-      __builtin_amdgcn_global_load_lds(kt + 16 * chunk_a, dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vt + 16 * chunk_a, dst + kTileBytes, 16, 0, 0);
+      const char* kt = fr ? ic.kf + (size_t)(uint32_t)(j - ic.a0) * fstride : ic.kc + ((size_t)(uint32_t)j << 8);
+      const char* vt = kt + (fr ? ic.dvf : ic.dvc);
+      __builtin_amdgcn_global_load_lds(kt + 16 * chunk_a, dk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vt + 16 * chunk_a, dv, 16, 0, 0);
     }
   };
   auto issue = [&](auto jc) __attribute__((always_inline)) {
@@ -1631,12 +1641,17 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
     const int nq = a1 - a0;
     const int h = hk * gg + min(wid, gg - 1);
     uint8_t* dst = q_lds + wid * (kQT * 256);
+    // (the lane's offsets are recomputed here rather than kept live across
+    // the loop: a uniform base plus a 32-bit lane offset per load)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const char* qb = (const char*)(qp + ((size_t)i * fresh_rows * Hq + h) * kD);
 #pragma unroll
     for (int v = 0; v < QLD; ++v) {
-      const int r = 4 * v + (lane >> 4);
-      const int k = (lane & 15) ^ (r & 15);
-      const uint16_t* src = qp + (((size_t)i * fresh_rows + max(min(r, nq - 1), 0)) * Hq + h) * kD;
-      __builtin_amdgcn_global_load_lds((const char*)src + 16 * k, dst + v * 1024, 16, 0, 0);
+      const int r = 4 * v + (ln >> 4);
+      const int k = (ln & 15) ^ (r & 15);
+      const uint32_t off = (uint32_t)(max(min(r, nq - 1), 0) * Hq * kD * 2 + 16 * k);
+      __builtin_amdgcn_global_load_lds(qb + off, dst + v * 1024, 16, 0, 0);
     }
   };
   // The same number of loads with next to nothing to fetch: every lane
