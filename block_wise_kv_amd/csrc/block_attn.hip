@@ -1164,29 +1164,34 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(AttnArgs a) {
   const uint32_t off_f = (uint32_t)(row_a * a.Hkv * 256 + 16 * chunk_a);
   const size_t fstride = (size_t)a.Hkv * 256;
   const char* kc_row0 = (const char*)kcp + ((size_t)g.i * a.Hkv + g.hk) * a.sq.Lcap * 256;
-  const char* vc_row0 = (const char*)vcp + ((size_t)g.i * a.Hkv + g.hk) * a.sq.Lcap * 256;
   const char* kf_row0 = (const char*)knp + ((size_t)g.i * a.fresh_rows * a.Hkv + g.hk) * 256;
-  const char* vf_row0 = (const char*)vnp + ((size_t)g.i * a.fresh_rows * a.Hkv + g.hk) * 256;
+  const long long dvc = (const char*)vcp - (const char*)kcp, dvf = (const char*)vnp - (const char*)knp;
+  typedef __attribute__((address_space(3))) void* LdsV;
   auto issue = [&](int q, auto jc) __attribute__((always_inline)) {
-    uint8_t* dst = set_ptr(jc) + wid * 1024;
-    // (hidden from alias analysis: the compiler otherwise takes the reads of
-    // the other ring sets in this round as depending on these loads and
-    // waits for all of them; the explicit waits order every hand-off)
+    // The destination as a plain LDS address, hidden from alias analysis:
+    // the compiler otherwise takes the reads of the other ring sets in this
+    // round as depending on these loads and waits for all of them (the
+    // explicit waits order every hand-off)
+    uint32_t dst = lds_addr(set_ptr(jc)) + wid * 1024;
     asm volatile("" : "+s"(dst));
+    const LdsV dk = (LdsV)(uintptr_t)dst, dv = (LdsV)(uintptr_t)(dst + kTileBytes);
     const int t0 = g.kb + q * kKT;
+    // (branch-free tests: a whole tile is in the cache unless it overlaps
+    // [a0, a1), and in the fresh rows if it lies inside [a0, a1))
     const bool whole = t0 + kKT <= g.ke;
-    const bool in_cache = whole && (t0 + kKT <= g.a0 || t0 >= g.a1);
-    const bool in_fresh = whole && t0 >= g.a0 && t0 + kKT <= g.a1;
-    if (in_cache || in_fresh) {
-      const char* kt = in_cache ? kc_row0 + (size_t)t0 * 256 : kf_row0 + (size_t)(t0 - g.a0) * fstride;
-      const char* vt = in_cache ? vc_row0 + (size_t)t0 * 256 : vf_row0 + (size_t)(t0 - g.a0) * fstride;
+    const bool overlaps = (unsigned)(t0 - (g.a0 - kKT + 1)) < (unsigned)(g.a1 - g.a0 + kKT - 1);
+    const bool inside = (g.a1 - g.a0 >= kKT) & ((unsigned)(t0 - g.a0) <= (unsigned)(g.a1 - g.a0 - kKT));
+    const bool in_cache = whole & !overlaps;
+    if (whole & (!overlaps | inside)) {
+      const char* kt = in_cache ? kc_row0 + ((size_t)(uint32_t)t0 << 8) : kf_row0 + (size_t)(uint32_t)(t0 - g.a0) * fstride;
+      const char* vt = kt + (in_cache ? dvc : dvf);
       const uint32_t off = in_cache ? off_c : off_f;
-      __builtin_amdgcn_global_load_lds(kt + off, dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vt + off, dst + kTileBytes, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kt + off, dk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vt + off, dv, 16, 0, 0);
     } else {
       const int j = min(t0 + row_a, g.ke - 1);
-      __builtin_amdgcn_global_load_lds((const char*)kv_row(a, knp, kcp, g, j, kD) + 16 * chunk_a, dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const char*)kv_row(a, vnp, vcp, g, j, kD) + 16 * chunk_a, dst + kTileBytes, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const char*)kv_row(a, knp, kcp, g, j, kD) + 16 * chunk_a, dk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const char*)kv_row(a, vnp, vcp, g, j, kD) + 16 * chunk_a, dv, 16, 0, 0);
     }
   };
 
