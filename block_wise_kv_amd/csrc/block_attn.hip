@@ -1464,11 +1464,13 @@ struct StreamCursor {
   long long dvc, dvf;   // V minus K: the same rows of the cached and fresh V
 };
 
-template <int NR>
+template <int NR, bool LOADER>
 __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArgs a) {
   constexpr int SET = 2 * kTileBytes;
-  constexpr int DPR = 2;   // ring loads per wave per tile
-  constexpr int QLD = 8;   // Q-prefetch loads per wave (32 rows x 256 bytes)
+  constexpr int NLD = LOADER ? 8 : 1;  // four-row groups of a tile one loading wave moves
+  constexpr int DPR = 2 * NLD;         // ring loads per loading wave per tile
+  constexpr int QLD = 8;               // Q-prefetch loads per wave (32 rows x 256 bytes)
+  constexpr int kLoaderWave = kGqaWaves - 1;
   static_assert(NR == 4, "four ring sets");
   // (the ring sets' larger alignment places them first, in the low 64 KB of
   // LDS, where their base fits a read's immediate offset)
@@ -1590,25 +1592,22 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
   }
   StreamCursor cc = ic;  // compute cursor
 
-  // K/V tile at the issue cursor into ring set J: wave w moves rows 4 w +
-  // [0, 4) of K and of V (one 1 KB LDS-DMA load each); this lane moves the
-  // 16-byte chunk that belongs at its LDS position under the ring swizzle.
-  // Rows past the part (and every tile once the cursor is past the range)
-  // re-read the part's last row, so every step issues the same loads.
-  const int row_a = 4 * wid + (lane >> 4);
-  const int chunk_a = (lane & 15) ^ ring_swizzle(row_a);
+  // K/V tile at the issue cursor into ring set J, as 1 KB LDS-DMA loads of
+  // four rows each: row group v is rows 4 v + [0, 4) of K and of V, and this
+  // lane moves the 16-byte chunk that belongs at its LDS position under the
+  // ring swizzle.  Wave w moves group w; with a loader wave, that wave moves
+  // all eight.  Rows past the part (and every tile once the cursor is past
+  // the range) re-read the part's last row, so every step issues the same
+  // loads.
   const size_t fstride = (size_t)Hkv * 256;
-  const uint32_t off_c = (uint32_t)(row_a * 256 + 16 * chunk_a);
-  const uint32_t off_f = (uint32_t)(row_a * Hkv * 256 + 16 * chunk_a);
   typedef __attribute__((address_space(3))) void* LdsV;
   auto issue_tile = [&](auto jc, int tile) __attribute__((always_inline)) {
     // The destination as a plain LDS address, hidden from alias analysis:
     // the compiler otherwise takes the reads of the other ring sets in this
     // step as depending on these loads and waits for all of them (the
-    // explicit waits above order every hand-off)
-    uint32_t dst = lds_addr(set_ptr(jc)) + wid * 1024;
+    // explicit waits order every hand-off)
+    uint32_t dst = lds_addr(set_ptr(jc)) + (LOADER ? 0 : wid * 1024);
     asm volatile("" : "+s"(dst));
-    const LdsV dk = (LdsV)(uintptr_t)dst, dv = (LdsV)(uintptr_t)(dst + kTileBytes);
     const int t0 = tile * kKT;
     // (branch-free tests: a whole tile is in the cache unless it overlaps
     // [a0, a1), and in the fresh rows if it lies inside [a0, a1))
@@ -1619,16 +1618,26 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
     if (whole & (!overlaps | inside)) {
       const char* kt = in_cache ? ic.kc + ((size_t)(uint32_t)t0 << 8) : ic.kf + (size_t)(uint32_t)(t0 - ic.a0) * fstride;
       const char* vt = kt + (in_cache ? ic.dvc : ic.dvf);
-      const uint32_t off = in_cache ? off_c : off_f;
-      __builtin_amdgcn_global_load_lds(kt + off, dk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vt + off, dv, 16, 0, 0);
+#pragma unroll
+      for (int v = 0; v < NLD; ++v) {
+        const int row = 4 * (LOADER ? v : wid) + (lane >> 4);
+        const int chunk = (lane & 15) ^ ring_swizzle(row);
+        const uint32_t off = (uint32_t)(row * (in_cache ? 256 : Hkv * 256) + 16 * chunk);
+        __builtin_amdgcn_global_load_lds(kt + off, (LdsV)(uintptr_t)(dst + v * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + off, (LdsV)(uintptr_t)(dst + v * 1024 + kTileBytes), 16, 0, 0);
+      }
     } else {
-      const int j = min(t0 + row_a, ic.ke - 1);
-      const bool fr = (unsigned)(j - ic.a0) < (unsigned)(ic.a1 - ic.a0);
-      const char* kt = fr ? ic.kf + (size_t)(uint32_t)(j - ic.a0) * fstride : ic.kc + ((size_t)(uint32_t)j << 8);
-      const char* vt = kt + (fr ? ic.dvf : ic.dvc);
-      __builtin_amdgcn_global_load_lds(kt + 16 * chunk_a, dk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vt + 16 * chunk_a, dv, 16, 0, 0);
+#pragma unroll
+      for (int v = 0; v < NLD; ++v) {
+        const int row = 4 * (LOADER ? v : wid) + (lane >> 4);
+        const int chunk = (lane & 15) ^ ring_swizzle(row);
+        const int j = min(t0 + row, ic.ke - 1);
+        const bool fr = (unsigned)(j - ic.a0) < (unsigned)(ic.a1 - ic.a0);
+        const char* kt = fr ? ic.kf + (size_t)(uint32_t)(j - ic.a0) * fstride : ic.kc + ((size_t)(uint32_t)j << 8);
+        const char* vt = kt + (fr ? ic.dvf : ic.dvc);
+        __builtin_amdgcn_global_load_lds(kt + 16 * chunk, (LdsV)(uintptr_t)(dst + v * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + 16 * chunk, (LdsV)(uintptr_t)(dst + v * 1024 + kTileBytes), 16, 0, 0);
+      }
     }
   };
   auto issue = [&](auto jc) __attribute__((always_inline)) {
@@ -1864,6 +1873,90 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
     else
       prefetch_none();
   };
+
+  if constexpr (LOADER) {
+    // With a loader wave (g < 8: wave 7 has no query head), that wave alone
+    // moves the ring: per step it waits for its own loads of tile x + 1,
+    // meets the others at the barrier and refills the set tile x - 1 used
+    // with tile x + 3.  The compute waves issue no ring loads: their only
+    // vector-memory operations are their own Q prefetches and output
+    // stores, so they wait for nothing at the ring's barriers but their
+    // LDS reads, and the stores at a segment's end hold back no ring wait.
+    if (wid == kLoaderWave) {
+      issue(std::integral_constant<int, 0>{});
+      advance(ic);
+      issue(std::integral_constant<int, 1>{});
+      advance(ic);
+      issue(std::integral_constant<int, 2>{});
+      advance(ic);
+      wait_vm<(NR - 2) * DPR, false>();
+      ring_barrier();
+      auto lstep = [&](auto jc) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        wait_vm<(NR - 3) * DPR, false>();
+        ring_barrier();
+        issue(std::integral_constant<int, (J + NR - 1) % NR>{});
+        advance(ic);
+      };
+      for (int qd = (int)(hi - lo) / NR; qd > 0; --qd) {
+        lstep(std::integral_constant<int, 0>{});
+        lstep(std::integral_constant<int, 1>{});
+        lstep(std::integral_constant<int, 2>{});
+        lstep(std::integral_constant<int, 3>{});
+      }
+      wait_vm<0, false>();
+      return;
+    }
+    auto cstep = [&](auto jc) __attribute__((always_inline)) {
+      constexpr int J = decltype(jc)::value;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's reads of the set to be refilled are done
+      ring_barrier();
+      if (cc.left <= 0) return;
+      const bool more = J < NR - 1 || cc.t + 1 < cc.te;
+      const bool keys = cc.t * kKT < cc.L;
+      if (live && more && (cc.t + 1) * kKT < cc.L)
+        stage_s(set_ptr(std::integral_constant<int, (J + 1) % NR>{}), Sb[(J + 1) & 1]);
+      if (live && keys) stage_pv(set_ptr(jc), cc.t * kKT, cc.ke, Sb[J & 1]);
+      if (more) advance(cc);
+    };
+    auto cboundary = [&]() __attribute__((always_inline)) {
+      if (cc.left > 0 && cc.t + 1 == cc.te) {
+        wait_vm<0, false>();  // the next segment's Q, prefetched at least a quad ago
+        finish(first);
+        reset();
+        first = false;
+        if (cc.left <= 1) {
+          cc.left = 0;
+        } else {
+          advance(cc);
+          read_q(cc.a1 - cc.a0);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // q_lds read before the next prefetch lands
+          if (live) stage_s(set_ptr(std::integral_constant<int, 0>{}), Sb[0]);
+          int i2, hk2;
+          if (live && next_seg(i2, hk2)) prefetch_q(i2, hk2);
+        }
+      }
+    };
+    if (live) prefetch_q(cc.i, cc.hk);
+    ring_barrier();
+    wait_vm<0, false>();
+    read_q(cc.a1 - cc.a0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (live) stage_s(ring0, Sb[0]);
+    {
+      int i2, hk2;
+      if (live && next_seg(i2, hk2)) prefetch_q(i2, hk2);
+    }
+    for (int qd = (int)(hi - lo) / NR; qd > 0; --qd) {
+      cstep(std::integral_constant<int, 0>{});
+      cstep(std::integral_constant<int, 1>{});
+      cstep(std::integral_constant<int, 2>{});
+      cstep(std::integral_constant<int, 3>{});
+      cboundary();
+    }
+    wait_vm<0, false>();
+    return;
+  }
 
   // prologue: Q of the first segment and tiles 0..2 in flight; then Q in
   // registers, S^T of tile 0, the next segment's Q prefetched
@@ -2234,8 +2327,8 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, int dtype, in
   if (dtype == 0 && d == kD) {
     const dim3 grid((unsigned)p.grid), block(kThreads);
     if (p.qt_per_wg == 16) {
-      const hipError_t e =
-          launch_kernel(attn_gqa_stream_kernel<4>, grid, dim3(kGqaThreads), 0, st, ev.start, (hipEvent_t) nullptr, a);
+      auto* kern = a.g < kGqaWaves ? attn_gqa_stream_kernel<4, true> : attn_gqa_stream_kernel<4, false>;
+      const hipError_t e = launch_kernel(kern, grid, dim3(kGqaThreads), 0, st, ev.start, (hipEvent_t) nullptr, a);
       if (e != hipSuccess) return e;
       return launch_kernel(attn_stream_merge_kernel, dim3((unsigned)(a.sq.b * a.Hkv)), dim3(kGqaThreads), 0, st,
                            (hipEvent_t) nullptr, ev.stop, a);

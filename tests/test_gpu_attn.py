@@ -266,6 +266,7 @@ VARIANTS = [
     ("c3like_dual", "bf16", 2, 28, 4, 128, [1024, 1024], 1024, 32, [5, 5], "dual"),
     ("c3like_prefix", "bf16", 2, 28, 4, 128, [1024, 1024], 1024, 32, [20, 20], "prefix"),
     ("gqa7_ragged", "bf16", 3, 14, 2, 128, [37, 100, 5], 96, 32, [0, 2, 1], "dual"),
+    ("gqa8_ragged", "bf16", 3, 16, 2, 128, [37, 100, 5], 96, 32, [0, 2, 1], "dual"),
     ("block4_gqa", "bf16", 2, 8, 2, 128, [13, 40], 16, 4, [3, 0], "dual"),
     ("none_gqa", "bf16", 2, 6, 3, 128, [17, 70], 32, 16, [0, 1], "none"),
     ("mha_prefix", "bf16", 2, 4, 4, 128, [130, 64], 160, 32, [1, 2], "prefix"),
@@ -278,7 +279,8 @@ VARIANTS = [
 def test_kernel_variants(case, qt, wgs):
     # every attention kernel (split-key, LDS ring with 2 or 4 query tiles per
     # workgroup, 8-wave LDS ring with one per wave, the 8-wave ring over the
-    # batch's tile stream) and key split on the same inputs
+    # batch's tile stream, with a loader wave when g < 8) and key split on
+    # the same inputs
     import block_wise_kv_amd as fd
     name, dt, b, hq, hkv, d, P, G, B, k, mode = case
     s = shape_custom(name, dt, b, hq, hkv, d, P, G, B, k, 64, cfg_id=52)
