@@ -1479,7 +1479,8 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[SET];
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[SET];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kGqaWaves * kQT * 256];  // each wave's next Q tile
-  __shared__ __attribute__((aligned(16))) uint8_t q_sink[kGqaWaves * 1024];      // never read (see prefetch_none)
+  __shared__ __attribute__((aligned(16))) uint8_t q_sink[LOADER ? 16 : kGqaWaves * 1024];  // never read (see prefetch_none)
+  __shared__ __attribute__((aligned(16))) uint8_t o_stage[LOADER ? kGqaWaves * 4096 : 16];  // finish's staging
   auto set_ptr = [&](auto jc) __attribute__((always_inline)) -> uint8_t* {
     constexpr int J = decltype(jc)::value % NR;
     if constexpr (J == 0) return ring0;
@@ -1761,48 +1762,81 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
   // The end of the compute cursor's part: the output rows when the part is
   // the whole segment, else the partial (O, m, l: fp16 O with a power-of-two
   // row scale) in slot (w, first ? 0 : 1): a workgroup's first segment holds
-  // its range start, a later cut segment its range end.  Stores straight
-  // from the accumulator layout (lane (lq, hh): row lq, head dims 32 dt +
-  // 8 q4 + 4 hh + [0, 4)).
+  // its range start, a later cut segment its range end.  Lane (lq, hh) holds
+  // row lq, head dims 32 dt + 8 q4 + 4 hh + [0, 4).  With a loader wave, O
+  // goes through this wave's 4 KB of o_stage, half the head dims at a time
+  // (16-byte unit 4 (dt % 2) + q4 of the 128-byte half row at unit ^ (lq &
+  // 7)), so that each global store writes eight whole 128-byte half rows;
+  // stores straight from the accumulator layout touch 32 rows each.
   auto finish = [&](bool first) __attribute__((always_inline)) {
     if (!live) return;
     const int h = cc.hk * gg + wid;
     const int nq = cc.a1 - cc.a0;
     const float l_col = xor_combine<32>(l_run, [](float x, float y) { return x + y; });
-    if (cc.tb == 0 && cc.te == cc.n) {
-      if (lq < nq) {
-        const float inv = 1.f / l_col;
-        uint16_t* orow = outp + (((size_t)cc.i * fresh_rows + lq) * Hq + h) * kD;
+    const bool whole = cc.tb == 0 && cc.te == cc.n;
+    float inv = 0.f;
+    int e = 0;
+    if (whole) {
+      inv = 1.f / l_col;
+    } else {
+      float amax = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            uint2 u;
-            u.x = pack_bf16x2(O[dt][4 * r4 + 0] * inv, O[dt][4 * r4 + 1] * inv);
-            u.y = pack_bf16x2(O[dt][4 * r4 + 2] * inv, O[dt][4 * r4 + 3] * inv);
-            *(uint2*)(orow + 32 * dt + 8 * r4 + 4 * hh) = u;
-          }
-      }
-      return;
+        for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(O[dt][r]));
+      amax = xor_combine<32>(amax, [](float x, float y) { return fmaxf(x, y); });
+      e = __builtin_amdgcn_frexp_expf(amax) - 15;  // amax < 2^(e + 15)
     }
-    float amax = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(O[dt][r]));
-    amax = xor_combine<32>(amax, [](float x, float y) { return fmaxf(x, y); });
-    const int e = __builtin_amdgcn_frexp_expf(amax) - 15;  // amax < 2^(e + 15)
-    uint8_t* part = partp + ((size_t)(2 * w + (first ? 0 : 1)) * kGqaWaves + wid) * kPart16Bytes;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        uint2 u;
+    // four values of O as 8 bytes: bf16 O / l, or fp16 O 2^-e
+    auto pack4 = [&](int dt, int q4) __attribute__((always_inline)) -> uint2 {
+      uint2 u;
+      if (whole) {
+        u.x = pack_bf16x2(O[dt][4 * q4 + 0] * inv, O[dt][4 * q4 + 1] * inv);
+        u.y = pack_bf16x2(O[dt][4 * q4 + 2] * inv, O[dt][4 * q4 + 3] * inv);
+      } else {
         u.x = pack_f16x2(__builtin_amdgcn_ldexpf(O[dt][4 * q4], -e), __builtin_amdgcn_ldexpf(O[dt][4 * q4 + 1], -e));
         u.y = pack_f16x2(__builtin_amdgcn_ldexpf(O[dt][4 * q4 + 2], -e), __builtin_amdgcn_ldexpf(O[dt][4 * q4 + 3], -e));
-        *(uint2*)(part + lq * 256 + 2 * (32 * dt + 8 * q4 + 4 * hh)) = u;
       }
-    if (hh == 0) {
+      return u;
+    };
+    uint16_t* obase = outp + ((size_t)cc.i * fresh_rows * Hq + h) * kD;
+    uint8_t* part = partp + ((size_t)(2 * w + (first ? 0 : 1)) * kGqaWaves + wid) * kPart16Bytes;
+    if constexpr (LOADER) {
+      uint8_t* wbuf = o_stage + wid * 4096;
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) {
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *(uint2*)(wbuf + lq * 128 + 16 * ((4 * d2 + q4) ^ (lq & 7)) + 8 * hh) = pack4(2 * hd + d2, q4);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // (the reads below are of other lanes' writes)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 8 * v + (lane >> 3), k = lane & 7;
+          const uint4 x = *(const uint4*)(wbuf + row * 128 + 16 * (k ^ (row & 7)));
+          if (whole) {
+            if (row < nq) *(uint4*)(obase + (size_t)row * Hq * kD + 64 * hd + 8 * k) = x;
+          } else {
+            *(uint4*)(part + row * 256 + 128 * hd + 16 * k) = x;
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read back before the next half is written
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint2 u = pack4(dt, q4);
+          if (whole) {
+            if (lq < nq) *(uint2*)(obase + (size_t)lq * Hq * kD + 32 * dt + 8 * q4 + 4 * hh) = u;
+          } else {
+            *(uint2*)(part + lq * 256 + 2 * (32 * dt + 8 * q4 + 4 * hh)) = u;
+          }
+        }
+    }
+    if (!whole && hh == 0) {
       float* hdr = (float*)(part + kQT * kD * 2);
       hdr[lq] = m_ref;
       hdr[kQT + lq] = l_col;
