@@ -2057,12 +2057,17 @@ __global__ __launch_bounds__(kGqaThreads) void attn_stream_merge_kernel(AttnArgs
   const int nq = a1 - a0;
   const int h = hk * a.g + wid;
   const float c = a.scale_log2;
-  const int row = lane & 31, half = lane >> 5;
-  float M = -INFINITY, Lsum = 0.f;
-  float acc[64];
+  // Lane l merges, for v = 0..7, the 16-byte piece k = l % 16 (head dims
+  // 8 k + [0, 8)) of row 4 v + l / 16, so each load and store moves four
+  // whole 256-byte rows; lane r < 32 keeps row r's running (M, L) and hands
+  // the row's factors to the lanes holding its pieces.
+  const int k = lane & 15, rq = lane >> 4;
+  float M = -INFINITY, Lsum = 0.f;  // of row `lane` (lanes < 32)
+  float acc[8][8];
 #pragma unroll
-  for (int k = 0; k < 64; ++k) acc[k] = 0.f;
-  const int col0 = 64 * half;
+  for (int v = 0; v < 8; ++v)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[v][t] = 0.f;
 #pragma unroll 1
   for (int ub = u0; ub <= u1; ub += 2) {
     float4 x[2][8];
@@ -2073,50 +2078,52 @@ __global__ __launch_bounds__(kGqaThreads) void attn_stream_merge_kernel(AttnArgs
       const int slot = (u == u0 && stream_lo(u, T, Gn) < seg0) ? 1 : 0;
       const uint8_t* part = (const uint8_t*)a.part + ((size_t)(2 * u + slot) * kGqaWaves + wid) * kPart16Bytes;
 #pragma unroll
-      for (int v = 0; v < 8; ++v) x[e][v] = *(const float4*)(part + row * 256 + 2 * col0 + 16 * v);
+      for (int v = 0; v < 8; ++v) x[e][v] = *(const float4*)(part + (4 * v + rq) * 256 + 16 * k);
       const float* hdr = (const float*)(part + kQT * kD * 2);
-      mp[e] = hdr[row];
-      lp[e] = hdr[kQT + row];
-      sp[e] = hdr[2 * kQT + row];
+      const int r = lane & 31;
+      mp[e] = hdr[r];
+      lp[e] = hdr[kQT + r];
+      sp[e] = hdr[2 * kQT + r];
     }
     if (ub + 1 > u1) mp[1] = -INFINITY;  // a re-read part adds nothing
+    // row factors (lane r < 32 for row r; lanes 32..63 hold copies)
     const float Mn = fmaxf(M, fmaxf(mp[0], mp[1]));
     const float fo = exp2_fast((M - Mn) * c);
-    Lsum *= fo;
-#pragma unroll
-    for (int k = 0; k < 64; ++k) acc[k] *= fo;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float fn = exp2_fast((mp[e] - Mn) * c);
-      Lsum = fmaf(lp[e], fn, Lsum);
-      const float ws = fn * sp[e];
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const uint32_t wv[4] = {__float_as_uint(x[e][v].x), __float_as_uint(x[e][v].y), __float_as_uint(x[e][v].z),
-                                __float_as_uint(x[e][v].w)};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float lo2, hi2;
-          unpack_f16x2(wv[k], lo2, hi2);
-          acc[8 * v + 2 * k] = fmaf(lo2, ws, acc[8 * v + 2 * k]);
-          acc[8 * v + 2 * k + 1] = fmaf(hi2, ws, acc[8 * v + 2 * k + 1]);
-        }
-      }
-    }
+    const float f0 = exp2_fast((mp[0] - Mn) * c), f1 = exp2_fast((mp[1] - Mn) * c);
+    Lsum = fmaf(lp[1], f1, fmaf(lp[0], f0, Lsum * fo));
+    const float w0 = f0 * sp[0], w1 = f1 * sp[1];
     M = Mn;
-  }
-  if (row < nq) {
-    const float inv = 1.f / Lsum;
-    uint16_t* orow = (uint16_t*)a.out + (((size_t)i * a.fresh_rows + row) * a.Hq + h) * kD + col0;
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
-      uint4 u;
-      u.x = pack_bf16x2(acc[8 * v + 0] * inv, acc[8 * v + 1] * inv);
-      u.y = pack_bf16x2(acc[8 * v + 2] * inv, acc[8 * v + 3] * inv);
-      u.z = pack_bf16x2(acc[8 * v + 4] * inv, acc[8 * v + 5] * inv);
-      u.w = pack_bf16x2(acc[8 * v + 6] * inv, acc[8 * v + 7] * inv);
-      *(uint4*)(orow + 8 * v) = u;
+      const int src = 4 * v + rq;
+      const float fov = __shfl(fo, src, 64), w0v = __shfl(w0, src, 64), w1v = __shfl(w1, src, 64);
+      const float4 xs[2] = {x[0][v], x[1][v]};
+      float lo0[4], hi0[4], lo1[4], hi1[4];
+      const uint32_t u0w[4] = {__float_as_uint(xs[0].x), __float_as_uint(xs[0].y), __float_as_uint(xs[0].z),
+                               __float_as_uint(xs[0].w)};
+      const uint32_t u1w[4] = {__float_as_uint(xs[1].x), __float_as_uint(xs[1].y), __float_as_uint(xs[1].z),
+                               __float_as_uint(xs[1].w)};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        unpack_f16x2(u0w[t], lo0[t], hi0[t]);
+        unpack_f16x2(u1w[t], lo1[t], hi1[t]);
+        acc[v][2 * t] = fmaf(lo1[t], w1v, fmaf(lo0[t], w0v, acc[v][2 * t] * fov));
+        acc[v][2 * t + 1] = fmaf(hi1[t], w1v, fmaf(hi0[t], w0v, acc[v][2 * t + 1] * fov));
+      }
     }
+  }
+  const float inv = 1.f / Lsum;
+  uint16_t* obase = (uint16_t*)a.out + ((size_t)i * a.fresh_rows * a.Hq + h) * kD;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int row = 4 * v + rq;
+    const float iv = __shfl(inv, row, 64);
+    uint4 u;
+    u.x = pack_bf16x2(acc[v][0] * iv, acc[v][1] * iv);
+    u.y = pack_bf16x2(acc[v][2] * iv, acc[v][3] * iv);
+    u.z = pack_bf16x2(acc[v][4] * iv, acc[v][5] * iv);
+    u.w = pack_bf16x2(acc[v][6] * iv, acc[v][7] * iv);
+    if (row < nq) *(uint4*)(obase + (size_t)row * a.Hq * kD + 8 * k) = u;
   }
 }
 
