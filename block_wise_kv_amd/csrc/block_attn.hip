@@ -1441,9 +1441,14 @@ __device__ __forceinline__ long long uniform_ll(long long v) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long long)v >> 32));
   return (long long)(((unsigned long long)hi << 32) | lo);
 }
-// The ranges are cut in whole quads of 4 tiles: with TQ = T / 4 quads,
+// The stream: each segment (sequence, KV head) is its tiles padded to whole
+// quads of 4, after kStreamPhantom units that stand for the fixed cost of
+// entering and finishing a segment (a segment switch costs about as much as
+// a quad of tiles), so that the ranges balance work rather than tile counts.
+// The ranges are cut in whole quads: with TQ = T / 4 quads of the stream,
 // range u is quads [u TQ / G, (u + 1) TQ / G).  stream_lo is a range's
-// first tile; stream_owner the range holding tile x.
+// first unit; stream_owner the range holding unit x.
+constexpr int kStreamPhantom = 4;
 __device__ __forceinline__ long long stream_lo(int u, long long T, int G) {
   return (long long)u * (T / kStreamQuad) / G * kStreamQuad;
 }
@@ -1519,11 +1524,12 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
 
   // ---- the partition (every wave computes it; the results are uniform).
   // With fewer quads than workgroups only the first TQ take part, so every
-  // range holds at least one quad and consecutive owners are consecutive
-  // workgroups (attn_stream_merge_kernel's part count relies on it).
+  // range holds at least one quad and consecutive owners of a segment's
+  // tiles are consecutive workgroups (attn_stream_merge_kernel's part count
+  // relies on it); a range of phantom units alone has no tiles.
   long long total = 0;
   for (int i0 = 0; i0 < b; i0 += 64) {
-    const int n = i0 + lane < b ? tiles_of_len((plens ? plens[i0 + lane] : Pu) + Gl) : 0;
+    const int n = i0 + lane < b ? tiles_of_len((plens ? plens[i0 + lane] : Pu) + Gl) + kStreamPhantom : 0;
     total += __shfl(wave_scan_incl(n), 63, 64);
   }
   const long long T = uniform_ll(total * a.Hkv);
@@ -1531,20 +1537,33 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
   const int Gn = (int)((long long)gridDim.x < TQ ? (long long)gridDim.x : TQ);
   if (w >= Gn) return;
   const long long lo = stream_lo(w, T, Gn), hi = stream_lo(w + 1, T, Gn);
-  int i_lo = 0;
-  long long base = 0;  // global index of sequence i_lo's first tile
-  for (int i0 = 0; i0 < b; i0 += 64) {
-    const bool in = i0 + lane < b;
-    const int n = in ? tiles_of_len((plens ? plens[i0 + lane] : Pu) + Gl) : 0;
-    const int incl = wave_scan_incl(n);
-    const uint64_t m = __ballot(in && base + (long long)Hkv * incl > lo);
-    if (m) {
-      const int f = __ffsll((unsigned long long)m) - 1;
-      i_lo = i0 + f;
-      base += (long long)Hkv * __shfl(incl - n, f, 64);
-      break;
+  // the sequences holding units lo and hi - 1, and the stream index of
+  // their first units
+  int i_lo = 0, i_hi = 0;
+  long long base = 0, base_hi = 0;
+  {
+    long long acc = 0;
+    bool found_lo = false;
+    for (int i0 = 0; i0 < b; i0 += 64) {
+      const bool in = i0 + lane < b;
+      const int n = in ? tiles_of_len((plens ? plens[i0 + lane] : Pu) + Gl) + kStreamPhantom : 0;
+      const int incl = wave_scan_incl(n);
+      const uint64_t m_lo = __ballot(in && acc + (long long)Hkv * incl > lo);
+      if (!found_lo && m_lo) {
+        const int f = __ffsll((unsigned long long)m_lo) - 1;
+        i_lo = i0 + f;
+        base = acc + (long long)Hkv * __shfl(incl - n, f, 64);
+        found_lo = true;
+      }
+      const uint64_t m_hi = __ballot(in && acc + (long long)Hkv * incl > hi - 1);
+      if (m_hi) {
+        const int f = __ffsll((unsigned long long)m_hi) - 1;
+        i_hi = i0 + f;
+        base_hi = acc + (long long)Hkv * __shfl(incl - n, f, 64);
+        break;
+      }
+      acc += (long long)Hkv * __shfl(incl, 63, 64);
     }
-    base += (long long)Hkv * __shfl(incl, 63, 64);
   }
 
   // segment geometry of a cursor that has just entered segment (i, hk) at tile t
@@ -1581,17 +1600,27 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
     }
   };
   i_lo = uniform_i(i_lo);
+  i_hi = uniform_i(i_hi);
   base = uniform_ll(base);
+  base_hi = uniform_ll(base_hi);
   StreamCursor ic;  // issue cursor, three tiles ahead of the compute cursor
   {
-    const int n0 = tiles_of_len(prompt_of(i_lo) + Gl);
+    const int nv0 = tiles_of_len(prompt_of(i_lo) + Gl) + kStreamPhantom;
+    const int nv1 = tiles_of_len(prompt_of(i_hi) + Gl) + kStreamPhantom;
+    const int o = (int)((lo - base) % nv0);  // a multiple of 4: 0 is the phantom quad
     ic.i = i_lo;
-    ic.hk = (int)((lo - base) / n0);
-    ic.t = (int)((lo - base) % n0);
-    ic.left = (int)(hi - lo);
-    enter(ic);
+    ic.hk = (int)((lo - base) / nv0);
+    ic.t = o < kStreamPhantom ? 0 : o - kStreamPhantom;
+    // the range's tiles: its units less the phantoms of the segments that
+    // start in it (those after the first segment's, and that one's if the
+    // range starts at it)
+    const int seg_lo = i_lo * Hkv + ic.hk, seg_hi = i_hi * Hkv + (int)((hi - 1 - base_hi) / nv1);
+    ic.left = (int)(hi - lo) - kStreamPhantom * (seg_hi - seg_lo + (o == 0 ? 1 : 0));
   }
+  if (ic.left <= 0) return;  // phantom units alone
+  enter(ic);
   StreamCursor cc = ic;  // compute cursor
+  const int n_quads = ic.left / NR;
 
   // K/V tile at the issue cursor into ring set J, as 1 KB LDS-DMA loads of
   // four rows each: row group v is rows 4 v + [0, 4) of K and of V, and this
@@ -1932,7 +1961,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
         issue(std::integral_constant<int, (J + NR - 1) % NR>{});
         advance(ic);
       };
-      for (int qd = (int)(hi - lo) / NR; qd > 0; --qd) {
+      for (int qd = n_quads; qd > 0; --qd) {
         lstep(std::integral_constant<int, 0>{});
         lstep(std::integral_constant<int, 1>{});
         lstep(std::integral_constant<int, 2>{});
@@ -1981,7 +2010,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
       int i2, hk2;
       if (live && next_seg(i2, hk2)) prefetch_q(i2, hk2);
     }
-    for (int qd = (int)(hi - lo) / NR; qd > 0; --qd) {
+    for (int qd = n_quads; qd > 0; --qd) {
       cstep(std::integral_constant<int, 0>{});
       cstep(std::integral_constant<int, 1>{});
       cstep(std::integral_constant<int, 2>{});
@@ -2013,7 +2042,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
     else
       prefetch_none();
   }
-  for (int qd = (int)(hi - lo) / NR; qd > 0; --qd) {
+  for (int qd = n_quads; qd > 0; --qd) {
     step(std::integral_constant<int, 0>{});
     step(std::integral_constant<int, 1>{});
     step(std::integral_constant<int, 2>{});
@@ -2039,7 +2068,7 @@ __global__ __launch_bounds__(kGqaThreads) void attn_stream_merge_kernel(AttnArgs
   const int b = a.sq.b;
   long long total = 0, before = 0;
   for (int i0 = 0; i0 < b; i0 += 64) {
-    const int n = i0 + lane < b ? seq_tiles(a, i0 + lane) : 0;
+    const int n = i0 + lane < b ? seq_tiles(a, i0 + lane) + kStreamPhantom : 0;
     total += __shfl(wave_scan_incl(n), 63, 64);
     const int nb = i0 + lane < i ? n : 0;
     before += __shfl(wave_scan_incl(nb), 63, 64);
@@ -2048,8 +2077,10 @@ __global__ __launch_bounds__(kGqaThreads) void attn_stream_merge_kernel(AttnArgs
   const long long TQ = T / kStreamQuad;
   const int Gn = (int)((long long)kNumCUs < TQ ? (long long)kNumCUs : TQ);
   const int n_i = seq_tiles(a, i);
-  const long long seg0 = uniform_ll(before * a.Hkv + (long long)hk * n_i);
-  const int u0 = stream_owner(seg0, T, Gn), u1 = stream_owner(seg0 + n_i - 1, T, Gn);
+  // the segment's first unit (its phantom quad) and its tiles
+  const long long seg0 = uniform_ll(before * a.Hkv + (long long)hk * (n_i + kStreamPhantom));
+  const long long t0 = seg0 + kStreamPhantom;
+  const int u0 = stream_owner(t0, T, Gn), u1 = stream_owner(t0 + n_i - 1, T, Gn);
   if (u0 == u1) return;  // written whole by its workgroup
   const int P = seq_prompt(a.sq, i);
   int a0, a1;
