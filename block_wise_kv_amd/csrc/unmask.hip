@@ -607,19 +607,30 @@ __global__ __launch_bounds__(kUT) void unmask_kernel(UnmaskArgs a) {
       }
       fold<N, kU>(acc, x, it);
     };
-    // The first two iterations are requested before the mask byte is looked
-    // at, and the first runs whatever it says (an unmasked row reduces it and
-    // discards the result), so nothing between these loads and the loop
-    // waits for the mask.
-    if (n_it > 0) {
-      // mask byte first: loads return in order, so it is in before va
-      const int mv = *mptr;
-      __builtin_amdgcn_sched_barrier(0);
-      load(va, 0);
-      load(vb, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      masked = __builtin_amdgcn_readfirstlane(mv) != 0;
-      const int n_run = masked ? n_it : 1;
+    // Small grids: the first two iterations are requested before the mask
+    // byte is looked at, and the first runs whatever it says (an unmasked
+    // row reduces it and discards the result), so nothing between these
+    // loads and the loop waits for the mask.  With a thousand workgroups or
+    // more, those waiting for their mask byte are covered by the others and
+    // the bytes matter more: the byte is read (scalar) before any load, and
+    // an unmasked row loads nothing.
+    const bool mask_first = gridDim.x * gridDim.y * gridDim.z >= 1024u;
+    if (n_it > 0 && mask_first) masked = load_mask_byte(mptr) != 0;
+    if (n_it > 0 && (!mask_first || masked)) {
+      int n_run = n_it;
+      if (mask_first) {
+        load(va, 0);
+        load(vb, 1);
+      } else {
+        // mask byte first: loads return in order, so it is in before va
+        const int mv = *mptr;
+        __builtin_amdgcn_sched_barrier(0);
+        load(va, 0);
+        load(vb, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        masked = __builtin_amdgcn_readfirstlane(mv) != 0;
+        n_run = masked ? n_it : 1;
+      }
       // va holds iteration it and vb iteration it + 1.  The last one or two
       // iterations are reduced after the loop, so no load is issued that
       // only the code after the loop would wait for (its registers are
@@ -635,7 +646,7 @@ __global__ __launch_bounds__(kUT) void unmask_kernel(UnmaskArgs a) {
       }
       reduce(va, it);
       if (it + 1 < n_run) reduce(vb, it + 1);
-    } else {
+    } else if (n_it == 0) {
       masked = load_mask_byte(mptr) != 0;  // no full vector: only the scalar tail below
     }
     // vocab entries past the last full vector of the chunk (fewer than W)
