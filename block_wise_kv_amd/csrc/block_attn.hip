@@ -2066,6 +2066,10 @@ __global__ __launch_bounds__(kGqaThreads) void attn_stream_merge_kernel(AttnArgs
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wid >= a.g) return;
   const int b = a.sq.b;
+  // this sequence's prompt length and block index, loaded together with the
+  // partition's prompt lengths (one memory round trip for both)
+  const int P = seq_prompt(a.sq, i);
+  const int kblk = seq_block(a.sq, i);
   long long total = 0, before = 0;
   for (int i0 = 0; i0 < b; i0 += 64) {
     const int n = i0 + lane < b ? seq_tiles(a, i0 + lane) + kStreamPhantom : 0;
@@ -2076,15 +2080,14 @@ __global__ __launch_bounds__(kGqaThreads) void attn_stream_merge_kernel(AttnArgs
   const long long T = uniform_ll(total * a.Hkv);
   const long long TQ = T / kStreamQuad;
   const int Gn = (int)((long long)kNumCUs < TQ ? (long long)kNumCUs : TQ);
-  const int n_i = seq_tiles(a, i);
+  const int n_i = ((P + a.sq.G + kKT - 1) / kKT + kStreamQuad - 1) / kStreamQuad * kStreamQuad;  // seq_tiles
   // the segment's first unit (its phantom quad) and its tiles
   const long long seg0 = uniform_ll(before * a.Hkv + (long long)hk * (n_i + kStreamPhantom));
   const long long t0 = seg0 + kStreamPhantom;
   const int u0 = stream_owner(t0, T, Gn), u1 = stream_owner(t0 + n_i - 1, T, Gn);
   if (u0 == u1) return;  // written whole by its workgroup
-  const int P = seq_prompt(a.sq, i);
   int a0, a1;
-  fresh_range(a.mode, P, a.sq.G, a.sq.B, seq_block(a.sq, i), a0, a1);
+  fresh_range(a.mode, P, a.sq.G, a.sq.B, kblk, a0, a1);
   const int nq = a1 - a0;
   const int h = hk * a.g + wid;
   const float c = a.scale_log2;
