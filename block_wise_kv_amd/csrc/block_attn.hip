@@ -1527,9 +1527,11 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
   // range holds at least one quad and consecutive owners of a segment's
   // tiles are consecutive workgroups (attn_stream_merge_kernel's part count
   // relies on it); a range of phantom units alone has no tiles.
+  // (the first 64 sequences' lengths are loaded once for both passes)
+  const int n_first = lane < b ? tiles_of_len((plens ? plens[lane] : Pu) + Gl) + kStreamPhantom : 0;
   long long total = 0;
   for (int i0 = 0; i0 < b; i0 += 64) {
-    const int n = i0 + lane < b ? tiles_of_len((plens ? plens[i0 + lane] : Pu) + Gl) + kStreamPhantom : 0;
+    const int n = i0 == 0 ? n_first : i0 + lane < b ? tiles_of_len((plens ? plens[i0 + lane] : Pu) + Gl) + kStreamPhantom : 0;
     total += __shfl(wave_scan_incl(n), 63, 64);
   }
   const long long T = uniform_ll(total * a.Hkv);
@@ -1546,7 +1548,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_stream_kernel(AttnArg
     bool found_lo = false;
     for (int i0 = 0; i0 < b; i0 += 64) {
       const bool in = i0 + lane < b;
-      const int n = in ? tiles_of_len((plens ? plens[i0 + lane] : Pu) + Gl) + kStreamPhantom : 0;
+      const int n = i0 == 0 ? n_first : in ? tiles_of_len((plens ? plens[i0 + lane] : Pu) + Gl) + kStreamPhantom : 0;
       const int incl = wave_scan_incl(n);
       const uint64_t m_lo = __ballot(in && acc + (long long)Hkv * incl > lo);
       if (!found_lo && m_lo) {
