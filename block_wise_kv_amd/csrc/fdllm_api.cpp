@@ -417,20 +417,21 @@ size_t fdllm_unmask_workspace(const fdllm_seq_desc* seq, int32_t vocab, int32_t 
 // ---- scratch of the allocation-free threshold unmask
 // (fdllm_unmask_threshold_static).  One array per device, held until the
 // process ends: the arrival counters first, at offsets that do not depend
-// on the batch (the finished-sequence counter at 0, the per-sequence
-// arrival counters at 256, the per-sequence done flags at 32 KB: counters
-// that must read zero never overlap a word another call left non-zero),
-// then the vocabulary-chunk partials.  The kernels reset every counter they
+// on the batch (the finished-sequence counter at 0, the per-sequence done
+// flags at 256, the per-sequence arrival counters, one per 128-byte line,
+// at 64 KB: counters that must read zero never overlap a word another call
+// left non-zero), then the vocabulary-chunk partials.  The kernels reset every counter they
 // use, so after one clear per device the array stays ready for the next
 // call.  Calls that overlap on one device share it and race.
 namespace {
 constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
-constexpr size_t kStaticCounterBytes = (size_t)64 << 10;
+constexpr size_t kStaticCounterBytes = (size_t)576 << 10;
 constexpr int kStaticMaxBatch = 4096;
-constexpr size_t kStaticSeqCntOffset = 256;
-constexpr size_t kStaticDoneFlagOffset = (size_t)32 << 10;
-static_assert(kStaticSeqCntOffset + 4 * (size_t)kStaticMaxBatch <= kStaticDoneFlagOffset, "counter layout");
-static_assert(kStaticDoneFlagOffset + 8 * (size_t)kStaticMaxBatch <= kStaticCounterBytes, "counter layout");
+constexpr size_t kStaticDoneFlagOffset = 256;
+constexpr size_t kStaticSeqCntOffset = (size_t)64 << 10;
+static_assert(kStaticDoneFlagOffset + 8 * (size_t)kStaticMaxBatch <= kStaticSeqCntOffset, "counter layout");
+static_assert(kStaticSeqCntOffset + 4 * (size_t)kSeqCntStride * kStaticMaxBatch <= kStaticCounterBytes,
+              "counter layout");
 constexpr int kMaxDevices = 64;
 }  // namespace
 

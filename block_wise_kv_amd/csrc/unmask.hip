@@ -344,7 +344,7 @@ __device__ void unmask_finalize_wave(const UnmaskArgs& a, int i, int start, cons
       const int k = a.sq.bidx[i];
       if (k + 1 < a.sq.G / a.sq.B) a.sq.bidx[i] = k + 1;
     }
-    a.seq_cnt[i] = 0u;
+    a.seq_cnt[(size_t)i * kSeqCntStride] = 0u;
   }
   if (!want_list) return;
   // the last sequence to finish writes the ascending list of finished ones
@@ -491,7 +491,7 @@ __device__ void unmask_finalize(const UnmaskArgs& a, int i, int start, const Row
       const int k = a.sq.bidx[i];
       if (k + 1 < a.sq.G / a.sq.B) a.sq.bidx[i] = k + 1;
     }
-    a.seq_cnt[i] = 0u;
+    a.seq_cnt[(size_t)i * kSeqCntStride] = 0u;
     s_done = done;
     s_count = 0;
     if (want_list && b <= kBitsSeqs) {
@@ -704,7 +704,7 @@ __global__ __launch_bounds__(kUT) void unmask_kernel(UnmaskArgs a) {
   }
 
   // the last of the sequence's B x nchunk workgroups finalises it
-  if (!block_arrive(&a.seq_cnt[i], (unsigned)(B * a.nchunk), &s_flag)) return;
+  if (!block_arrive(&a.seq_cnt[(size_t)i * kSeqCntStride], (unsigned)(B * a.nchunk), &s_flag)) return;
   const ChunkMerge merge{make_rsrc(a.part + (size_t)i * B * a.nchunk), a.nchunk, B};
   if (B <= 64 && a.sq.b <= kBitsSeqs) {
     if (tid < 64) unmask_finalize_wave(a, i, start, merge);
@@ -818,13 +818,13 @@ hipError_t launch_lmhead_finalize(const UnmaskArgs& a, const UnmaskPartial* part
                        n_vwg);
 }
 
-// Workgroups the vocab split aims for (the environment variable
-// FDLLM_UNMASK_TARGET_WGS overrides the default for tuning).
+// Workgroups the vocab split aims for when the environment variable
+// FDLLM_UNMASK_TARGET_WGS sets it (for tuning; 0 when unset).
 static long unmask_target_workgroups() {
   static long v = [] {
     const char* e = getenv("FDLLM_UNMASK_TARGET_WGS");
-    long t = e ? atol(e) : 512;
-    return t > 0 ? t : 512;
+    const long t = e ? atol(e) : 0;
+    return t > 0 ? t : 0;
   }();
   return v;
 }
@@ -836,10 +836,17 @@ UnmaskPlan plan_unmask(int dtype, int V, int rows) {
   UnmaskPlan p{};
   const int W = dtype == 0 ? 8 : 4;
   const int iter_elems = kU * kUT * W;           // one workgroup iteration
-  // split rows so that about the target number of workgroups covers the
-  // batch (at most one chunk per iteration and at most 16 chunks per row)
+  // Chunks per row: by default two, and four for batches of at most 64 rows
+  // (one or two blocks), whose few workgroups per sequence stream too little
+  // at two.  Measured per call on MI355X with 126k-152k logits per row (1,
+  // 2, 4 ... chunks): 32 rows 10.6 / 9.7 / 11.2 us at 2 / 4 / 16 chunks; 256
+  // rows 25.5 us at 2, 26.4 at 3, 27.0 at 4; 1024 rows 51 us at 1, 53 at 2;
+  // 2048 rows of which 59 % masked 89 / 84 / 86 us at 1 / 2 / 3.  A target
+  // workgroup count set for tuning overrides the rule (at most one chunk per
+  // iteration and at most 16 chunks per row).
   const long target = g_unmask_wgs > 0 ? g_unmask_wgs : unmask_target_workgroups();
-  const int want = (int)((target + rows - 1) / rows);
+  int want = rows <= 64 ? 4 : 2;
+  if (target > 0) want = (int)((target + rows - 1) / rows);
   const int by_iter = (V + iter_elems - 1) / iter_elems;
   int nchunk = want < by_iter ? want : by_iter;
   if (nchunk > kMaxChunks) nchunk = kMaxChunks;
@@ -856,9 +863,11 @@ UnmaskPlan plan_unmask(int dtype, int V, int rows) {
 // then the chunk partials.  Zeroed once; every counter is reset by its last
 // user, so the unmask calls and the fused LM-head calls of one batch can
 // share a workspace whatever their vocabulary split.
+static size_t unmask_seq_cnt_offset(int b) {
+  return (16 + (size_t)b * 8 + 127) & ~(size_t)127;  // after the global counter and the done flags
+}
 static size_t unmask_counter_bytes(int b) {
-  const size_t bytes = 16 + (size_t)b * 8 + (size_t)b * 4;  // global counter, done flags, sequence counters
-  return (bytes + 255) & ~(size_t)255;
+  return unmask_seq_cnt_offset(b) + (size_t)b * 4 * kSeqCntStride;  // one line per sequence counter
 }
 
 size_t unmask_workspace_bytes(int b, int B, int nchunk) {
@@ -870,7 +879,7 @@ void unmask_bind_workspace(UnmaskArgs& a, void* workspace) {
   char* w = (char*)workspace;
   a.glob = (uint64_t*)w;
   a.done_flag = (int32_t*)(w + 16);
-  a.seq_cnt = (uint32_t*)(w + 16 + (size_t)a.sq.b * 8);
+  a.seq_cnt = (uint32_t*)(w + unmask_seq_cnt_offset(a.sq.b));
   a.part = (UnmaskPartial*)(w + unmask_counter_bytes(a.sq.b));
 }
 

@@ -191,7 +191,7 @@ fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, in
  * array of the library (8 MiB per device, held until the process ends; the
  * first call on a device finds its address and clears its counters with a
  * fill kernel on `stream`).  Limits: batch <= 4096 and batch x block_size x
- * vocabulary chunks x 16 bytes <= 8 MiB - 64 KiB (a call beyond them returns
+ * vocabulary chunks x 16 bytes <= 8 MiB - 576 KiB (a call beyond them returns
  * FDLLM_ERR_UNSUPPORTED and launches nothing).  Every call on a device
  * shares that device's scratch: calls that overlap in time on one device
  * (different streams without ordering, or several host threads) race and
