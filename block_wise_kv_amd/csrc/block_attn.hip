@@ -64,6 +64,7 @@ constexpr int kPartFloats = kQT * kD + 2 * kQT;  // one split partial: O, m, l
 // m, l and the rows' power-of-two scales in fp32.
 constexpr int kPart16Bytes = kQT * kD * 2 + 3 * kQT * 4;
 constexpr int kMaxSplit = 8;           // key chunks per group
+constexpr int kCntStride = 32;         // uint32 per arrival counter: one 128-byte line each (atomics on one line serialise)
 constexpr int kVtStride = 36;          // bf16 per d-row of the split kernel's transposed V tile
 // Split kernel's wave-merge buffer: [4 waves][32 query rows][32 chunks of 4
 // floats]; chunk k of row r sits at k ^ red_swizzle(r), which keeps both the
@@ -590,7 +591,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(AttnArgs a) {
     st_coherent_b32(prs, kQT * kD * 2 + lq * 4, M);
     st_coherent_b32(prs, kQT * kD * 2 + (kQT + lq) * 4, Lsum);
   }
-  uint32_t* cnt = a.cnt + ((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt;
+  uint32_t* cnt = a.cnt + (((size_t)g.i * a.Hq + g.h) * a.n_qt + g.qt) * kCntStride;
   if (!block_arrive(cnt, (unsigned)g.n_act, &s_last)) return;
 
   // ---- last workgroup of this tile: merge the n_act split partials
@@ -1033,7 +1034,7 @@ __global__ __launch_bounds__(kThreads, (QT == 4 && NR <= 4) ? 2 : 1) void attn_r
     }
   }
   if (!split) return;
-  uint32_t* cnt = a.cnt + ((size_t)g.i * a.Hkv + g.hk) * a.n_grp + grp;
+  uint32_t* cnt = a.cnt + (((size_t)g.i * a.Hkv + g.hk) * a.n_grp + grp) * kCntStride;
   if (!block_arrive(cnt, (unsigned)g.n_act, &s_last)) return;
 
   // ---- last workgroup of this group: merge the n_act split partials of
@@ -2364,7 +2365,7 @@ AttnPlan plan_block_attn(int dtype, int b, int Hq, int Hkv, int d, int nq_max, i
 // fewer; the 8-wave ring uses none).
 size_t attn_counter_bytes(int b, int Hq, int nq_bound) {
   const size_t n = (size_t)b * Hq * ((nq_bound + kQT - 1) / kQT);
-  return (n * sizeof(uint32_t) + 255) & ~(size_t)255;
+  return (n * sizeof(uint32_t) * kCntStride + 255) & ~(size_t)255;
 }
 
 // Bytes of a workspace that serves every call of the geometry: the counters

@@ -268,10 +268,10 @@ def test_set_tuning_rejects_and_replans():
         fd.set_tuning()
     assert one == 0 and many > 0  # one key chunk needs no partials
     # the counter region (one 4-byte counter per sequence, head and query
-    # tile, rounded up to 256 bytes), then 8 key chunks of partials for 8 x
-    # 28 heads x 32 rows: O in fp16 (256 bytes per row), then m, l and the
-    # row scale in fp32
-    counters = (8 * 28 * 1 * 4 + 255) // 256 * 256
+    # tile, each on its own 128-byte line, rounded up to 256 bytes), then 8
+    # key chunks of partials for 8 x 28 heads x 32 rows: O in fp16 (256 bytes
+    # per row), then m, l and the row scale in fp32
+    counters = (8 * 28 * 1 * 128 + 255) // 256 * 256
     assert one8 == 0 and auto8 == counters + 8 * 28 * 8 * (32 * 128 * 2 + 3 * 32 * 4)
 
 
