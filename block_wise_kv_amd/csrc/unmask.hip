@@ -585,13 +585,16 @@ __global__ __launch_bounds__(kUT) void unmask_kernel(UnmaskArgs a) {
   bool masked;
   if (a.vec) {
     const int n_it = (nfull + kIterVec - 1) / kIterVec;
-    // Past the chunk the loads re-read its last vector, which stays in
-    // cache, so the loads in flight are the same on every path and reducing
-    // one buffer never waits for the other.
+    // Past the chunk the loads re-read its last vector, so the loads in
+    // flight are the same on every path and reducing one buffer never waits
+    // for the other.  The logits are read once: non-temporal loads.
     uint4 va[kU], vb[kU];
     auto load = [&](uint4 (&buf)[kU], int it) {
 #pragma unroll
-      for (int u = 0; u < kU; ++u) buf[u] = rv[min(it * kIterVec + u * kUT + tid, vlast)];
+      for (int u = 0; u < kU; ++u) {
+        const u32x4 w = __builtin_nontemporal_load((const u32x4*)(rv + min(it * kIterVec + u * kUT + tid, vlast)));
+        buf[u] = make_uint4(w.x, w.y, w.z, w.w);
+      }
     };
     auto reduce = [&](const uint4 (&buf)[kU], int it) {
       float x[N];
@@ -836,16 +839,18 @@ UnmaskPlan plan_unmask(int dtype, int V, int rows) {
   UnmaskPlan p{};
   const int W = dtype == 0 ? 8 : 4;
   const int iter_elems = kU * kUT * W;           // one workgroup iteration
-  // Chunks per row: by default two, and four for batches of at most 64 rows
-  // (one or two blocks), whose few workgroups per sequence stream too little
-  // at two.  Measured per call on MI355X with 126k-152k logits per row (1,
-  // 2, 4 ... chunks): 32 rows 10.6 / 9.7 / 11.2 us at 2 / 4 / 16 chunks; 256
-  // rows 25.5 us at 2, 26.4 at 3, 27.0 at 4; 1024 rows 51 us at 1, 53 at 2;
-  // 2048 rows of which 59 % masked 89 / 84 / 86 us at 1 / 2 / 3.  A target
-  // workgroup count set for tuning overrides the rule (at most one chunk per
-  // iteration and at most 16 chunks per row).
+  // Chunks per row: one, and four for batches of at most 64 rows (one or
+  // two blocks), whose few workgroups per sequence stream too little with
+  // one.  The logits are loaded non-temporally, which favours long
+  // streams per workgroup.  Measured per call on MI355X with 126k-152k
+  // logits per row: 32 rows 11.8 / 10.1 / 11.3 us at 2 / 4 / 8 chunks; 256
+  // rows 19.3 / 21.6 / 24.8 us at 1 / 2 / 4; 1024 rows 49.5 / 64 us at 1 /
+  // 4; 2048 rows of which 59 % masked 79 / 90 us at 1 / 4.  (With cached
+  // loads two chunks were best at 256 and 2048 rows: 25.5 and 84 us.)  A
+  // target workgroup count set for tuning overrides the rule (at most one
+  // chunk per iteration and at most 16 chunks per row).
   const long target = g_unmask_wgs > 0 ? g_unmask_wgs : unmask_target_workgroups();
-  int want = rows <= 64 ? 4 : 2;
+  int want = rows <= 64 ? 4 : 1;
   if (target > 0) want = (int)((target + rows - 1) / rows);
   const int by_iter = (V + iter_elems - 1) / iter_elems;
   int nchunk = want < by_iter ? want : by_iter;
