@@ -149,3 +149,55 @@ def test_unaligned_rows_scalar_path():
     say("edge unaligned")
     g, _ = run_unmask(s, None, tokens, mask, 0.7, ragged=True, logits_dev=view)
     compare_unmask(g, _ref(s, logits, tokens, mask, 0.7), s, label="unaligned")
+
+
+def _vpos(it, u, thread, e):
+    # vocab id of element e of the 16-byte vector that thread `thread` loads
+    # in slot u of iteration it of a row read whole (bf16: 8 logits per
+    # vector, 256 threads x 8 slots per iteration)
+    return 8 * (it * 2048 + u * 256 + thread) + e
+
+
+# (first, second) planted positions of an equal row maximum; the committed
+# token must be the lower one (the oracle's argmax)
+TIE_POSITIONS = [
+    (_vpos(0, 0, 5, 2), _vpos(0, 0, 5, 6)),      # one vector
+    (_vpos(0, 3, 7, 1), _vpos(4, 3, 7, 0)),      # one thread and slot, iterations 0 and 4
+    (_vpos(8, 1, 100, 5), _vpos(9, 0, 10, 4)),   # the last two iterations, thread 100 then 10
+    (_vpos(0, 0, 0, 7), _vpos(9, 2, 3, 0)),      # the first and the last iteration
+    (_vpos(2, 0, 8, 6), _vpos(2, 0, 9, 3)),      # neighbouring threads
+    (_vpos(1, 2, 11, 4), _vpos(1, 5, 11, 4)),    # one thread, slots 2 and 5
+    (152064 - 9, 152064 - 1),                    # the row's last vector
+    (_vpos(9, 1, 50, 3), None),                  # a single maximum in the last iteration
+]
+
+
+@pytest.mark.parametrize("chunks", [0, 4])
+def test_tied_maxima_take_the_lowest_index(chunks):
+    # Dream-7B vocabulary, 96 rows (read whole by default, or in 4 chunks):
+    # every row's maximum 64.0 (exact in bf16) is planted at positions that
+    # put the tie inside one thread's vector, across its iterations and
+    # slots, in the last two iterations and across threads.
+    s = shape_custom("ties", "bf16", 3, 1, 1, 8, [16, 40, 5], 64, 32, [0, 1, 0], 152064, cfg_id=62)
+    logits = make_logits(s, "peak")
+    for i in range(s.batch):
+        for t in range(s.block_size):
+            p1, p2 = TIE_POSITIONS[(i * s.block_size + t) % len(TIE_POSITIONS)]
+            logits[i, t, p1] = 64.0
+            if p2 is not None:
+                logits[i, t, p2] = 64.0
+    tokens, mask = make_decode_state(s, 32)
+    fd_tuning = __import__("block_wise_kv_amd").set_tuning
+    fd_tuning(unmask_wgs=4 * s.batch * s.block_size if chunks else 0)
+    try:
+        say(f"ties chunks={chunks or 1}")
+        g, _ = run_unmask(s, logits, tokens, mask, 0.3, ragged=True)
+    finally:
+        fd_tuning()
+    ref = _ref(s, logits, tokens, mask, 0.3)
+    compare_unmask(g, ref, s, label=f"ties {chunks}")
+    for i in range(s.batch):
+        start = int(s.prompt_lens[i]) + int(s.block_idxs[i]) * s.block_size
+        for t in range(s.block_size):
+            p1, _ = TIE_POSITIONS[(i * s.block_size + t) % len(TIE_POSITIONS)]
+            assert g["tokens"][i, start + t] == p1, (i, t)
