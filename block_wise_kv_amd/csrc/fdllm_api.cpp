@@ -543,6 +543,97 @@ fdllm_status run_unmask(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits
 }
 }  // namespace
 
+static_assert(kMaxRefreshLayers == FDLLM_MAX_REFRESH_LAYERS, "refresh layer limit");
+
+namespace {
+// fdllm_kv_refresh (one layer, `layers` false) and fdllm_kv_refresh_layers:
+// the same checks, then one launch over n_layers layers (host arrays of
+// per-layer device pointers).
+fdllm_status run_refresh(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode, int32_t n_layers,
+                         const void* const* k_src, const void* const* v_src, void* const* k_cache,
+                         void* const* v_cache, const int32_t* seq_ids, const int32_t* n_seq, void* stream,
+                         bool layers) {
+  SeqArgs sa;
+  int max_P;
+  fdllm_status st = check_seq(seq, sa, max_P);
+  if (st) return st;
+  st = check_attn_desc(attn, false);
+  if (st) return st;
+  if (mode < FDLLM_CACHE_NONE || mode > FDLLM_CACHE_DUAL)
+    return fail(FDLLM_ERR_INVALID_ARG, "mode %d is not a fdllm_cache_mode", mode);
+  if (seq_ids && !n_seq) return fail(FDLLM_ERR_INVALID_ARG, "seq_ids needs the device count n_seq");
+  if (layers && (n_layers < 1 || n_layers > kMaxRefreshLayers))
+    return fail(FDLLM_ERR_INVALID_ARG, "n_layers %d outside [1, %d]", n_layers, kMaxRefreshLayers);
+  if (layers && (!k_src || !v_src || !k_cache || !v_cache))
+    return fail(FDLLM_ERR_INVALID_ARG, "the per-layer pointer arrays must be non-NULL");
+  if (mode == FDLLM_CACHE_NONE) return ok();  // nothing is cached
+  for (int l = 0; l < n_layers; ++l) {
+    if (!k_src[l] || !v_src[l] || !k_cache[l] || !v_cache[l])
+      return layers ? fail(FDLLM_ERR_INVALID_ARG, "layer %d: k_src, v_src, k_cache and v_cache must be non-NULL", l)
+                    : fail(FDLLM_ERR_INVALID_ARG, "k_src, v_src, k_cache and v_cache must be non-NULL");
+    const void* ptrs[] = {k_src[l], v_src[l], k_cache[l], v_cache[l]};
+    for (const void* p : ptrs)
+      if (!aligned16(p)) return fail(FDLLM_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  }
+  const size_t es = attn->dtype == FDLLM_BF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)attn->head_dim * es;
+  if (row_bytes % 16 != 0) return fail(FDLLM_ERR_UNSUPPORTED, "head_dim * element size must be a multiple of 16");
+  size_t vpr = row_bytes / 16;
+  int shift = 0;
+  while ((1u << shift) < vpr) ++shift;
+  if ((1u << shift) != vpr) return fail(FDLLM_ERR_UNSUPPORTED, "head_dim * element size / 16 must be a power of two");
+  if ((((int64_t)seq->max_seq_len * attn->n_kv_heads) << shift) >= ((int64_t)1 << 31))
+    return fail(FDLLM_ERR_INVALID_ARG, "per-sequence cache too large");
+  const size_t cb = (size_t)seq->batch * attn->n_kv_heads * seq->max_seq_len * row_bytes;
+  // no cache may overlap another cache or any source (of any layer): the
+  // result would depend on the order of the stores
+  const void* dst[2 * kMaxRefreshLayers];
+  const void* src[2 * kMaxRefreshLayers];
+  for (int l = 0; l < n_layers; ++l) {
+    dst[2 * l] = k_cache[l];
+    dst[2 * l + 1] = v_cache[l];
+    src[2 * l] = k_src[l];
+    src[2 * l + 1] = v_src[l];
+  }
+  bool alias = false;
+  for (int x = 0; x < 2 * n_layers && !alias; ++x) {
+    for (int y = 0; y < 2 * n_layers && !alias; ++y) alias = ranges_overlap(dst[x], cb, src[y], cb);
+    for (int y = x + 1; y < 2 * n_layers && !alias; ++y) alias = ranges_overlap(dst[x], cb, dst[y], cb);
+  }
+  if (alias) return fail(FDLLM_ERR_INVALID_ARG, "caches must not alias the sources or each other");
+  st = debug_validate(sa, max_P, seq_ids, n_seq, stream);
+  if (st) return st;
+  RefreshArgs a{};
+  a.sq = sa;
+  a.mode = mode;
+  a.Hkv = attn->n_kv_heads;
+  a.row_vec_shift = shift;
+  a.hkv_div = make_fastdiv((uint32_t)attn->n_kv_heads);
+  a.seq_ids = seq_ids;
+  a.n_seq = n_seq;
+  const int max_rows = max_P + seq->gen_len;
+  hipError_t e;
+  if (!layers) {
+    a.k_src = (const uint4*)k_src[0];
+    a.v_src = (const uint4*)v_src[0];
+    a.k_cache = (uint4*)k_cache[0];
+    a.v_cache = (uint4*)v_cache[0];
+    e = launch_kv_refresh(a, max_rows, (hipStream_t)stream);
+  } else {
+    RefreshLayerPtrs p{};
+    for (int l = 0; l < n_layers; ++l) {
+      p.k_src[l] = (const uint4*)k_src[l];
+      p.v_src[l] = (const uint4*)v_src[l];
+      p.k_cache[l] = (uint4*)k_cache[l];
+      p.v_cache[l] = (uint4*)v_cache[l];
+    }
+    e = launch_kv_refresh_layers(a, p, n_layers, max_rows, (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "kv_refresh launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+}  // namespace
+
 extern "C" {
 
 fdllm_status fdllm_unmask_threshold(const fdllm_seq_desc* seq, int32_t vocab, int32_t logits_dtype,
@@ -634,53 +725,18 @@ fdllm_status fdllm_set_lmhead_tuning(int32_t vt) {
 fdllm_status fdllm_kv_refresh(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode,
                               const void* k_src, const void* v_src, void* k_cache, void* v_cache,
                               const int32_t* seq_ids, const int32_t* n_seq, void* stream) {
-  SeqArgs sa;
-  int max_P;
-  fdllm_status st = check_seq(seq, sa, max_P);
-  if (st) return st;
-  st = check_attn_desc(attn, false);
-  if (st) return st;
-  if (mode < FDLLM_CACHE_NONE || mode > FDLLM_CACHE_DUAL)
-    return fail(FDLLM_ERR_INVALID_ARG, "mode %d is not a fdllm_cache_mode", mode);
-  if (seq_ids && !n_seq) return fail(FDLLM_ERR_INVALID_ARG, "seq_ids needs the device count n_seq");
-  if (mode == FDLLM_CACHE_NONE) return ok();  // nothing is cached
-  if (!k_src || !v_src || !k_cache || !v_cache)
-    return fail(FDLLM_ERR_INVALID_ARG, "k_src, v_src, k_cache and v_cache must be non-NULL");
-  const void* ptrs[] = {k_src, v_src, k_cache, v_cache};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return fail(FDLLM_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
-  const size_t es = attn->dtype == FDLLM_BF16 ? 2 : 4;
-  const size_t row_bytes = (size_t)attn->head_dim * es;
-  if (row_bytes % 16 != 0) return fail(FDLLM_ERR_UNSUPPORTED, "head_dim * element size must be a multiple of 16");
-  size_t vpr = row_bytes / 16;
-  int shift = 0;
-  while ((1u << shift) < vpr) ++shift;
-  if ((1u << shift) != vpr) return fail(FDLLM_ERR_UNSUPPORTED, "head_dim * element size / 16 must be a power of two");
-  if ((((int64_t)seq->max_seq_len * attn->n_kv_heads) << shift) >= ((int64_t)1 << 31))
-    return fail(FDLLM_ERR_INVALID_ARG, "per-sequence cache too large");
-  const size_t cb = (size_t)seq->batch * attn->n_kv_heads * seq->max_seq_len * row_bytes;
-  if (ranges_overlap(k_cache, cb, k_src, cb) || ranges_overlap(k_cache, cb, v_src, cb) ||
-      ranges_overlap(v_cache, cb, k_src, cb) || ranges_overlap(v_cache, cb, v_src, cb) ||
-      ranges_overlap(k_cache, cb, v_cache, cb))
-    return fail(FDLLM_ERR_INVALID_ARG, "caches must not alias the sources or each other");
-  st = debug_validate(sa, max_P, seq_ids, n_seq, stream);
-  if (st) return st;
-  RefreshArgs a{};
-  a.sq = sa;
-  a.mode = mode;
-  a.Hkv = attn->n_kv_heads;
-  a.row_vec_shift = shift;
-  a.hkv_div = make_fastdiv((uint32_t)attn->n_kv_heads);
-  a.k_src = (const uint4*)k_src;
-  a.v_src = (const uint4*)v_src;
-  a.k_cache = (uint4*)k_cache;
-  a.v_cache = (uint4*)v_cache;
-  a.seq_ids = seq_ids;
-  a.n_seq = n_seq;
-  const int max_rows = max_P + seq->gen_len;
-  hipError_t e = launch_kv_refresh(a, max_rows, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(FDLLM_ERR_LAUNCH, "kv_refresh launch failed: %s", hipGetErrorString(e));
-  return ok();
+  const void* ks = k_src;
+  const void* vs = v_src;
+  void* kc = k_cache;
+  void* vc = v_cache;
+  return run_refresh(seq, attn, mode, 1, &ks, &vs, &kc, &vc, seq_ids, n_seq, stream, false);
+}
+
+fdllm_status fdllm_kv_refresh_layers(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode,
+                                     int32_t n_layers, const void* const* k_src, const void* const* v_src,
+                                     void* const* k_cache, void* const* v_cache, const int32_t* seq_ids,
+                                     const int32_t* n_seq, void* stream) {
+  return run_refresh(seq, attn, mode, n_layers, k_src, v_src, k_cache, v_cache, seq_ids, n_seq, stream, true);
 }
 
 fdllm_status fdllm_workspace_init(void* workspace, size_t bytes, void* stream) {

@@ -59,6 +59,17 @@ struct RefreshArgs {
   const int32_t* n_seq;
 };
 hipError_t launch_kv_refresh(const RefreshArgs& a, int max_rows, hipStream_t st);
+// The refresh of several layers in one launch: layer l (grid z) moves
+// k_src[l] / v_src[l] into k_cache[l] / v_cache[l] with RefreshArgs' geometry.
+constexpr int kMaxRefreshLayers = 64;
+struct RefreshLayerPtrs {
+  const uint4* k_src[kMaxRefreshLayers];
+  const uint4* v_src[kMaxRefreshLayers];
+  uint4* k_cache[kMaxRefreshLayers];
+  uint4* v_cache[kMaxRefreshLayers];
+};
+hipError_t launch_kv_refresh_layers(const RefreshArgs& a, const RefreshLayerPtrs& p, int n_layers, int max_rows,
+                                    hipStream_t st);
 
 // ------------------------------------------------------------------ unmask
 struct UnmaskPartial {      // per (sequence, row, vocab chunk)

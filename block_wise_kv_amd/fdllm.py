@@ -84,6 +84,9 @@ _SIGS = [
     ("fdllm_set_lmhead_tuning", ctypes.c_int32, [ctypes.c_int32]),
     ("fdllm_kv_refresh", ctypes.c_int32,
      [ctypes.POINTER(SeqDesc), ctypes.POINTER(AttnDesc), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
+    ("fdllm_kv_refresh_layers", ctypes.c_int32,
+     [ctypes.POINTER(SeqDesc), ctypes.POINTER(AttnDesc), ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
+      _P]),
     ("fdllm_workspace_init", ctypes.c_int32, [_P, ctypes.c_size_t, _P]),
     ("fdllm_set_debug", ctypes.c_int32, [ctypes.c_int32]),
     ("fdllm_set_timing_events", ctypes.c_int32, [_P, _P]),
@@ -296,6 +299,20 @@ def kv_refresh(seq: SeqDesc, mode: str, k_src, v_src, k_cache, v_cache, seq_ids=
     ad = attn_desc(0, k_src.shape[2], k_src.shape[3], _dtype_code(k_src))
     _check(lib().fdllm_kv_refresh(ctypes.byref(seq), ctypes.byref(ad), MODE[mode], _ptr(k_src), _ptr(v_src),
                                   _ptr(k_cache), _ptr(v_cache), _ptr(seq_ids), _ptr(n_seq), _stream(stream)))
+
+
+def kv_refresh_layers(seq: SeqDesc, mode: str, k_srcs, v_srcs, k_caches, v_caches, seq_ids=None, n_seq=None,
+                      stream=None):
+    """fdllm_kv_refresh_layers: one launch refreshing every layer l from k_srcs[l] / v_srcs[l] into
+    k_caches[l] / v_caches[l] (lists of tensors laid out as for kv_refresh)."""
+    n = len(k_srcs)
+    if not (len(v_srcs) == len(k_caches) == len(v_caches) == n):
+        raise ValueError("kv_refresh_layers needs the same number of k_srcs, v_srcs, k_caches and v_caches")
+    ad = attn_desc(0, k_srcs[0].shape[2], k_srcs[0].shape[3], _dtype_code(k_srcs[0])) if n else attn_desc(0, 1, 64, F32)
+    arr = lambda ts: (ctypes.c_void_p * max(n, 1))(*[_ptr(t) for t in ts])
+    ks, vs, kc, vc = arr(k_srcs), arr(v_srcs), arr(k_caches), arr(v_caches)
+    _check(lib().fdllm_kv_refresh_layers(ctypes.byref(seq), ctypes.byref(ad), MODE[mode], n, ks, vs, kc, vc,
+                                         _ptr(seq_ids), _ptr(n_seq), _stream(stream)))
 
 
 def set_debug(on: bool):

@@ -306,6 +306,27 @@ fdllm_status fdllm_kv_refresh(const fdllm_seq_desc* seq, const fdllm_attn_desc* 
                               const void* k_src, const void* v_src, void* k_cache, void* v_cache,
                               const int32_t* seq_ids, const int32_t* n_seq, void* stream);
 
+/* The refresh of several layers at one block boundary ([REV] review 4: the
+ * K/V of every layer are recomputed once a block is decoded) in one kernel
+ * launch: for l < n_layers, layer l's caches k_cache[l] / v_cache[l] get
+ * exactly what fdllm_kv_refresh(seq, attn, mode, k_src[l], v_src[l],
+ * k_cache[l], v_cache[l], seq_ids, n_seq, stream) writes.  The per-layer
+ * calls of a small refresh (a few finished sequences) each last about a
+ * launch and one memory round trip; one launch for all layers streams them
+ * at the full rate.
+ *   n_layers 1..FDLLM_MAX_REFRESH_LAYERS
+ *   k_src, v_src, k_cache, v_cache  HOST arrays of n_layers DEVICE pointers
+ *            (the caller keeps them; read during the call only), each laid
+ *            out as in fdllm_kv_refresh, 16-byte aligned.
+ * No cache may overlap another layer's cache or any layer's source
+ * (FDLLM_ERR_INVALID_ARG); sources may be shared.  Other arguments and
+ * errors as in fdllm_kv_refresh. */
+#define FDLLM_MAX_REFRESH_LAYERS 64
+fdllm_status fdllm_kv_refresh_layers(const fdllm_seq_desc* seq, const fdllm_attn_desc* attn, int32_t mode,
+                                     int32_t n_layers, const void* const* k_src, const void* const* v_src,
+                                     void* const* k_cache, void* const* v_cache, const int32_t* seq_ids,
+                                     const int32_t* n_seq, void* stream);
+
 /* ------------------------------------------------------------------ */
 /* utilities                                                           */
 /* ------------------------------------------------------------------ */

@@ -293,6 +293,23 @@ static void refresh_and_settings() {
   expect(fdllm_kv_refresh(&s, &a, FDLLM_CACHE_DUAL, P(0), P(256), P(512), P(768), (const int32_t*)P(1024), nullptr,
                           nullptr),
          FDLLM_ERR_INVALID_ARG, "refresh seq_ids without n_seq");
+  {
+    const void* ks[2] = {P(0), P(256)};
+    const void* vs[2] = {P(512), P(768)};
+    void* kc[2] = {P(1024), P(1280)};
+    void* vc[2] = {P(1536), P(1792)};
+    void* kc_alias[2] = {P(1024), P(256)};
+    expect(fdllm_kv_refresh_layers(&s, &a, FDLLM_CACHE_DUAL, 0, ks, vs, kc, vc, nullptr, nullptr, nullptr),
+           FDLLM_ERR_INVALID_ARG, "refresh_layers no layer");
+    expect(fdllm_kv_refresh_layers(&s, &a, FDLLM_CACHE_DUAL, 65, ks, vs, kc, vc, nullptr, nullptr, nullptr),
+           FDLLM_ERR_INVALID_ARG, "refresh_layers too many layers");
+    expect(fdllm_kv_refresh_layers(&s, &a, FDLLM_CACHE_DUAL, 2, nullptr, vs, kc, vc, nullptr, nullptr, nullptr),
+           FDLLM_ERR_INVALID_ARG, "refresh_layers NULL array");
+    expect(fdllm_kv_refresh_layers(&s, &a, FDLLM_CACHE_DUAL, 2, ks, vs, kc_alias, vc, nullptr, nullptr, nullptr),
+           FDLLM_ERR_INVALID_ARG, "refresh_layers cache on a source");
+    expect(fdllm_kv_refresh_layers(&s, &a, FDLLM_CACHE_NONE, 2, ks, vs, kc, vc, nullptr, nullptr, nullptr), FDLLM_OK,
+           "refresh_layers none");
+  }
   expect(fdllm_workspace_init(nullptr, 256, nullptr), FDLLM_ERR_INVALID_ARG, "workspace_init NULL");
   expect(fdllm_workspace_init(P(8), 256, nullptr), FDLLM_ERR_INVALID_ARG, "workspace_init misaligned");
   expect(fdllm_set_tuning(3, 0, 0), FDLLM_ERR_INVALID_ARG, "tuning qt 3");

@@ -240,6 +240,29 @@ def test_refresh_rejects_and_none_is_noop():
     assert st == 0
 
 
+def test_refresh_layers_rejects_and_none_is_noop():
+    L = fd.lib()
+    ad = F.attn_desc(0, 32, 128, F.BF16)
+    arr = lambda *ps: (ctypes.c_void_p * len(ps))(*ps)
+    # two layers: the caches of layer 1 are the sources of layer 0 shifted, all distinct
+    ks, vs = arr(P1, P5), arr(P2, P6)
+    kc, vc = arr(P3, P7), arr(P4, P7 + (1 << 35))
+    call = lambda n, *a, mode=2, seq=None: L.fdllm_kv_refresh_layers(
+        ctypes.byref(seq or _seq()), ctypes.byref(ad), mode, n, *a)
+    for n in (0, 65, -1):
+        assert call(n, ks, vs, kc, vc, None, None, None) == 1
+        assert "n_layers" in L.fdllm_last_error().decode()
+    assert call(2, None, vs, kc, vc, None, None, None) == 1
+    assert call(2, ks, vs, kc, vc, P1, None, None) == 1 and "n_seq" in L.fdllm_last_error().decode()
+    assert call(2, ks, vs, kc, arr(P4, None), None, None, None) == 1 and "layer 1" in L.fdllm_last_error().decode()
+    assert call(2, ks, vs, kc, arr(P4, P7 + 8), None, None, None) == 1 and "aligned" in L.fdllm_last_error().decode()
+    # a cache of one layer on another layer's source, or two layers sharing a cache
+    assert call(2, ks, vs, arr(P3, P1), vc, None, None, None) == 1 and "alias" in L.fdllm_last_error().decode()
+    assert call(2, ks, vs, arr(P3, P3), vc, None, None, None) == 1 and "alias" in L.fdllm_last_error().decode()
+    # sources may be shared between layers; no-cache mode keeps nothing
+    assert call(2, arr(P1, P1), arr(P2, P2), kc, vc, None, None, None, mode=0) == 0
+
+
 def test_workspace_init_rejects():
     L = fd.lib()
     assert L.fdllm_workspace_init(None, 64, None) == 1

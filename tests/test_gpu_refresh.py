@@ -1,6 +1,6 @@
-"""GPU parity: fdllm_kv_refresh against the oracle (bit-exact), and the
-full ragged step (28 x attention, one unmask, refresh of the finished
-sequences' 28 layer caches)."""
+"""GPU parity: fdllm_kv_refresh and fdllm_kv_refresh_layers against the
+oracle (bit-exact), and the full ragged step (28 x attention, one unmask,
+one refresh of the finished sequences' 28 layer caches)."""
 import numpy as np
 import pytest
 import torch
@@ -60,6 +60,37 @@ def test_refresh_modes(name, s, ragged, mode):
     assert np.array_equal(kc, rk) and np.array_equal(vc, rv)
 
 
+@pytest.mark.parametrize("subset", [False, True])
+@pytest.mark.parametrize("mode", ["dual", "prefix", "none"])
+@pytest.mark.parametrize("name,s,ragged", CASES, ids=[c[0] for c in CASES])
+def test_refresh_layers(name, s, ragged, mode, subset):
+    """fdllm_kv_refresh_layers: three layers in one launch, each layer with
+    its own sources and caches, equal to the oracle's per-layer refresh bit
+    for bit (rows it does not refresh keep their sentinels)."""
+    n_layers = 3
+    keep = []
+    seq = seq_for(s, ragged, keep)
+    ids_host = [s.batch - 1, 0][:s.batch] if subset else None
+    ids = n = None
+    if subset:
+        ids = torch.tensor(ids_host + [0] * (s.batch - len(ids_host)), dtype=torch.int32, device=DEV)
+        n = torch.tensor([len(ids_host)], dtype=torch.int32, device=DEV)
+    srcs = [make_refresh_src(s, variant=l) for l in range(n_layers)]
+    kc0, vc0 = _sentinel(s, s.dtype)
+    k_src = [to_dev(x[0], s.dtype) for x in srcs]
+    v_src = [to_dev(x[1], s.dtype) for x in srcs]
+    kcs = [to_dev(kc0 * (l + 1), s.dtype) for l in range(n_layers)]
+    vcs = [to_dev(vc0 * (l + 1), s.dtype) for l in range(n_layers)]
+    say(f"refresh layers {name} {mode} subset={subset}")
+    fd.kv_refresh_layers(seq, mode, k_src, v_src, kcs, vcs, ids, n)
+    torch.cuda.synchronize()
+    for l in range(n_layers):
+        rk, rv = refresh_ref(srcs[l][0], srcs[l][1], kc0 * (l + 1), vc0 * (l + 1), s.prompt_lens, s.gen_len,
+                             s.block_size, s.block_idxs, mode, seq_ids=ids_host)
+        assert np.array_equal(kcs[l].float().cpu().numpy(), rk), f"layer {l} K"
+        assert np.array_equal(vcs[l].float().cpu().numpy(), rv), f"layer {l} V"
+
+
 def test_refresh_subset_from_device_list():
     s = shape_custom("rs", "bf16", 5, 4, 2, 128, [10, 20, 30, 40, 50], 64, 16, [0, 1, 2, 3, 0], 64, cfg_id=72)
     ks, vs = make_refresh_src(s)
@@ -115,7 +146,7 @@ def test_c5_full_step_28_layers():
     # each layer owns its cache; layer l holds the same values scaled by a
     # power of two (exact in bf16), so every layer's output is distinct
     kcs = [kc0 * (2.0 ** -(l % 3)) for l in range(n_layers)]
-    vcs = [vc0 for _ in range(n_layers)]
+    vcs = [vc0.clone() for _ in range(n_layers)]
     ad = fd.attn_desc(28, 4, 128, fd.BF16)
     ws = fd.new_workspace(fd.block_attn_workspace(seq, ad, "dual", q.shape[1]))
     outs = [torch.empty_like(q) for _ in range(n_layers)]
@@ -131,12 +162,12 @@ def test_c5_full_step_28_layers():
     uws = fd.new_workspace(fd.unmask_workspace(seq, s.vocab, fd.BF16))
     srcs = make_refresh_src(s)
     k_src, v_src = to_dev(srcs[0], "bf16"), to_dev(srcs[1], "bf16")
-    say("c5 full step: 28 x attn + unmask + 28 x refresh(done)")
+    say("c5 full step: 28 x attn + unmask + one refresh of the done list's 28 layers")
     for l in range(n_layers):
         fd.block_attn(seq, "dual", q, kn, vn, kcs[l], vcs[l], outs[l], ws)
     fd.unmask_threshold(seq, lg, 0.7, tk, mk, nd, dp, None, ds, nn, uws, flags=fd.UNMASK_ADVANCE_BLOCK)
-    for l in range(n_layers):
-        fd.kv_refresh(seq, "dual", k_src, v_src, kcs[l], vcs[l], ds, nn)
+    # every layer's caches from the same full-forward sources (shared)
+    fd.kv_refresh_layers(seq, "dual", [k_src] * n_layers, [v_src] * n_layers, kcs, vcs, ds, nn)
     torch.cuda.synchronize()
     # attention of every sequence on layers 0-2 (the three distinct cache
     # scalings); layers 3..27 repeat them and must equal them bit for bit
@@ -159,12 +190,13 @@ def test_c5_full_step_28_layers():
     if not ref.tie_step.any() and not ref.tie_tau.any():
         assert done == list(ref.done_seqs)
     # refreshed sequences' caches equal the source on every layer; others untouched
-    ks_t = k_src.transpose(1, 2)
-    for l in (0, 13, 27):
+    ks_t, vs_t = k_src.transpose(1, 2), v_src.transpose(1, 2)
+    for l in range(n_layers):
         for i in range(s.batch):
             L = int(s.prompt_lens[i]) + s.gen_len
             if i in done:
-                assert torch.equal(kcs[l][i, :, :L], ks_t[i, :, :L])
+                assert torch.equal(kcs[l][i, :, :L], ks_t[i, :, :L]) and torch.equal(vcs[l][i, :, :L], vs_t[i, :, :L])
+                assert torch.equal(kcs[l][i, :, L:], (kc0[i] * (2.0 ** -(l % 3)))[:, L:])
             else:
-                assert torch.equal(kcs[l][i], kc0[i] * (2.0 ** -(l % 3)))
+                assert torch.equal(kcs[l][i], kc0[i] * (2.0 ** -(l % 3))) and torch.equal(vcs[l][i], vc0[i])
     say(f"  c5 step: {len(done)} sequences finished their block and were refreshed")
