@@ -1,7 +1,8 @@
 """HIP-graph replay of a decoding step built from every kernel variant.
 
 The split-key attention (in-kernel merge through arrival counters), the
-8-wave GQA ring with its merge kernel, the refresh, both unmask rules
+8-wave GQA ring with its merge kernel, the refresh (one layer, and two
+layers in one launch from the unmask's done list), both unmask rules
 (per-sequence arrival counters, the finished-sequence list and the block
 advance) and the fused LM head with its finalisation are captured once and
 replayed several times, with eager work and
@@ -49,6 +50,13 @@ class _Step:
         self.kc2, self.vc2 = d(self.inp2.k_cache), d(self.inp2.v_cache)
         ks, vs = make_refresh_src(self.s1, variant=1)
         self.ks1, self.vs1 = d(ks), d(vs)
+        # the done list of s2's unmask refreshes two layer caches in one launch
+        ks2, vs2 = make_refresh_src(self.s2, variant=2)
+        self.ks2, self.vs2 = d(ks2), d(vs2)
+        self.rkc_0 = [self.kc2.clone(), self.kc2.clone() * 0.5]
+        self.rvc_0 = [self.vc2.clone(), self.vc2.clone() * 2.0]
+        self.rkc = [t.clone() for t in self.rkc_0]
+        self.rvc = [t.clone() for t in self.rvc_0]
         self.out1 = torch.zeros_like(self.q1)
         self.out2 = torch.zeros_like(self.q2)
         ad1 = fd.attn_desc(4, 4, 128, fd.BF16)
@@ -93,7 +101,8 @@ class _Step:
     def restore(self):
         for dst, src in ((self.kc1, self.kc1_0), (self.vc1, self.vc1_0), (self.tk1, self.tk1_0),
                          (self.mk1, self.mk1_0), (self.tk2, self.tk2_0), (self.mk2, self.mk2_0),
-                         (self.bidx2, self.bidx2_0), (self.tk3, self.tk3_0), (self.mk3, self.mk3_0)):
+                         (self.bidx2, self.bidx2_0), (self.tk3, self.tk3_0), (self.mk3, self.mk3_0),
+                         *zip(self.rkc, self.rkc_0), *zip(self.rvc, self.rvc_0)):
             dst.copy_(src)
 
     def launch(self):
@@ -102,6 +111,8 @@ class _Step:
         fd.block_attn(self.seq2, "dual", self.q2, self.kn2, self.vn2, self.kc2, self.vc2, self.out2, self.ws2)
         fd.unmask_threshold(self.seq2, self.lg2, 0.7, self.tk2, self.mk2, self.nd2, self.dp2, self.cf2,
                             self.ds2, self.nn2, self.uws2, flags=fd.UNMASK_ADVANCE_BLOCK)
+        fd.kv_refresh_layers(self.seq2, "dual", [self.ks2] * 2, [self.vs2] * 2, self.rkc, self.rvc, self.ds2,
+                             self.nn2)
         fd.unmask_topk(self.seq1, self.lg1, 3, self.tk1, self.mk1, self.nd1, self.dp1, None, None, None,
                        self.uws1)
         fd.lmhead_unmask_threshold(self.seq3, self.lx, self.lwp, 3000, 0.6, self.tk3, self.mk3, self.nd3, self.dp3,
@@ -111,7 +122,7 @@ class _Step:
         return [t.clone() for t in (self.kc1, self.vc1, self.out1, self.out2, self.tk1, self.mk1, self.nd1,
                                     self.dp1, self.tk2, self.mk2, self.nd2, self.dp2, self.cf2, self.ds2,
                                     self.nn2, self.bidx2, self.tk3, self.mk3, self.nd3, self.dp3, self.ds3,
-                                    self.nn3)]
+                                    self.nn3, *self.rkc, *self.rvc)]
 
 
 def test_graph_replays_match_eager():
@@ -130,6 +141,19 @@ def test_graph_replays_match_eager():
     check_attn(ref[3].float().cpu().numpy().astype(np.float64), oracle_attn_subset(st.inp2, [1]), st.inp2,
                seqs=[1], label="graph step gqa")
     assert int(ref[14].item()) >= 1  # a sequence finished its block and is listed
+    # the one-launch refresh of the listed sequences' two layers: listed
+    # sequences' rows [0, L) hold the sources, the rest keep their values
+    done2 = [int(x) for x in ref[13].cpu().numpy()[:int(ref[14].item())]]
+    ks2_t, vs2_t = st.ks2.transpose(1, 2), st.vs2.transpose(1, 2)
+    for l in range(2):
+        kc_l, vc_l = ref[22 + l], ref[24 + l]
+        for i in range(st.s2.batch):
+            L = int(st.s2.prompt_lens[i]) + st.s2.gen_len
+            if i in done2:
+                assert torch.equal(kc_l[i, :, :L], ks2_t[i, :, :L]) and torch.equal(vc_l[i, :, :L], vs2_t[i, :, :L])
+                assert torch.equal(kc_l[i, :, L:], st.rkc_0[l][i, :, L:])
+            else:
+                assert torch.equal(kc_l[i], st.rkc_0[l][i]) and torch.equal(vc_l[i], st.rvc_0[l][i])
     # the fused LM head against the oracle: sequence 0 had nothing masked
     from oracle import lmhead_unmask_ref
     t3, m3 = st.tk3_0.cpu().numpy(), st.mk3_0.cpu().numpy()
