@@ -71,7 +71,7 @@ WORKLOADS = {
                     "gen 512, block 32, block index U{0..15} and U{1..32} masked rows per sequence, DualCache, "
                     "vocab 152064, calibrated confidences, tau 0.7; one step = 28 x block attention (one cache per layer) + 1 x threshold "
                     "unmask with block advance + refresh of the finished sequences' 28 layer caches (one launch)",
-               steps=50, warmup=10, layers=28, logit_sets=2),
+               steps=50, warmup=40, layers=28, logit_sets=2),
     "c2": dict(desc="LLaDA-8B-shaped layer: batch 1, 32 heads x 128 (MHA), prompt 512 + gen 256, block 32, "
                     "DualCache, block index 0..7 swept, tau in {0.7, 0.9, 1.0}, vocab 126464; "
                     "one block-step = refresh + attention + unmask",
